@@ -1,0 +1,69 @@
+"""The seeded generator: determinism, dtype rounding and the named workloads (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+
+
+@pytest.mark.parametrize("dtype,tdt", [(si.F16, torch.float16), (si.BF16, torch.bfloat16)])
+def test_rounding_matches_torch_round_to_nearest_even(dtype, tdt):
+    r = np.random.default_rng(0)
+    x = np.concatenate([r.standard_normal(20000).astype(np.float32) * 3,
+                        r.standard_normal(2000).astype(np.float32) * 1e4,
+                        np.array([0.0, -0.0, 1.0, 65504.0, 1e-6, -3.5], np.float32)])
+    bits = si.round_to_bits(x, dtype)
+    want = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, want)
+
+
+def test_bf16_ties_go_to_even():
+    one = np.float32(1.0)
+    half_ulp = np.float32(2.0 ** -8)  # bf16 has 7 stored mantissa bits
+    x = np.array([one + half_ulp, one + 3 * half_ulp, one + half_ulp * np.float32(1.0001)],
+                 np.float32)
+    assert si.round_to_bits(x, si.BF16).tolist() == [0x3F80, 0x3F82, 0x3F81]
+
+
+@pytest.mark.parametrize("dtype", [si.F16, si.BF16])
+def test_decode_is_exact(dtype):
+    r = np.random.default_rng(1)
+    bits = si.round_to_bits(r.standard_normal(5000).astype(np.float32), dtype)
+    back = si.round_to_bits(si.bits_to_f64(bits, dtype).astype(np.float32), dtype)
+    np.testing.assert_array_equal(bits, back)
+
+
+def test_same_seed_same_bits():
+    a = si.random_inputs(1, 2, 1, 33, 64, si.BF16, 9, causal=True)
+    b = si.random_inputs(1, 2, 1, 33, 64, si.BF16, 9, causal=True)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)):
+        np.testing.assert_array_equal(x, y)
+    c = si.random_inputs(1, 2, 1, 33, 64, si.BF16, 10, causal=True)
+    assert not np.array_equal(a.q, c.q)
+
+
+def test_named_workloads():
+    w = si.WORKLOADS
+    assert list(w) == si.WORKLOAD_ORDER and len(w) == 5
+    c5 = w["varlen16_h16_d128_causal_bf16"]
+    assert c5.seq_lens == (5664, 6695, 685, 6717, 4113, 4470, 5352, 2707, 8035, 926, 2646,
+                           3456, 4899, 3649, 1518, 859)
+    assert c5.seqlen == 62391 and c5.cu_seqlens()[-1] == 62391
+    assert all(512 <= n <= 8192 for n in c5.seq_lens)
+    c3 = w[si.HEADLINE]
+    assert math.isclose(c3.flops(), 32 * 4 * 16384 ** 2 * 128 / 2)
+    assert math.isclose(c3.scale, 0.08838834764831843)
+    assert w["gqa_b1_hq32_hkv8_n32768_d128_causal_bf16"].heads_kv == 8
+
+
+def test_row_sample_has_edges_and_stays_in_range():
+    w = si.WORKLOADS["varlen16_h16_d128_causal_bf16"]
+    rows = si.sample_rows(w, 1 / 4096, seed=1)
+    cu = w.cu_seqlens()
+    toks = {t for _, _, t in rows}
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        assert s0 in toks and s1 - 1 in toks
+    assert all(0 <= t < w.seqlen and 0 <= h < w.heads_q and b == 0 for b, h, t in rows)
+    assert rows == si.sample_rows(w, 1 / 4096, seed=1)
