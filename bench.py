@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the exact tiled attention forward pass (libfa) on one MI355X.
+
+One step = one full forward pass (every query block, head and K/V tile) over the workload's
+seeded synthetic inputs, already resident in device memory. Prints one JSON line:
+TFLOP/s by the convention 4*N^2*d per (batch, head), halved when causal; the fraction of the
+MI355X dense MFMA peak of the input type; and the fp64 CPU oracle timed on a bounded, seeded
+sample of query rows of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import seeded_inputs as si  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak, N=16K d=128 causal bf16"
+# MI355X published dense matrix peaks (TFLOP/s), per input type
+MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0}
+KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = ROOT / "profiles" / f"fa_fwd_{workload}_traffic.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, on seeded query rows until the time budget is spent."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    q, k, v = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    rows = si.sample_rows(w, 1 / 64, seed=1234)
+    order = np.random.default_rng(99).permutation(len(rows))
+    rows = [rows[i] for i in order]
+    cu = inp.cu_seqlens
+    starts = cu[:-1] if cu is not None else None
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done < len(rows) and time.perf_counter() - t0 < seconds:
+        chunk = rows[done:done + 32]
+        oracle.attention_rows(q, k, v, w.scale, w.causal, chunk, cu_seqlens=cu)
+        for _, _, i in chunk:
+            if cu is not None:
+                s = int(np.searchsorted(starts, i, side="right")) - 1
+                while cu[s + 1] <= i:
+                    s += 1
+                s0, s1 = int(cu[s]), int(cu[s + 1])
+            else:
+                s0, s1 = 0, w.seqlen
+            keys = (i - s0 + 1) if w.causal else (s1 - s0)
+            flops += 4.0 * keys * w.head_dim
+        done += len(chunk)
+    elapsed = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                   if p.get("user_api") == "blas"] or [1])
+    total_rows = w.batch * w.heads_q * w.seqlen
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} seeded query rows of {total_rows} ({done / total_rows:.2e} of the "
+                   f"workload), {elapsed:.1f} s, fp64, same FLOP convention per row "
+                   f"(4*keys*d)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=si.HEADLINE, choices=si.WORKLOAD_ORDER)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_tiled_attention_39_amd as fa
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = si.WORKLOADS[args.workload]
+    inp = si.workload_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == si.BF16 else torch.float16
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(tdt).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
+    max_seqlen = w.max_seqlen() if w.varlen else None
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal, cu_seqlens=cu,
+                  max_seqlen=max_seqlen)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()  # fa_fwd launches on this stream
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = float(np.mean(launch_ms))
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+
+    # quick parity on a few seeded rows (the tests cover parity in depth)
+    import oracle
+    rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
+    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
+                                           cu_seqlens=inp.cu_seqlens)
+    del qf, kf, vf
+    idx = tuple(np.array(rows).T)
+    o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    o_gpu = si.bits_to_f64(o_bits[idx], w.dtype)
+    lse_gpu = lse.cpu().numpy().astype(np.float64)[idx]
+    parity = {
+        "rows": len(rows),
+        "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
+        "max_lse_err": float((np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1)).max()),
+    }
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, see seeded_inputs.py)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "heads_q": w.heads_q,
+            "heads_kv": w.heads_kv,
+            "seqlen": w.seqlen,
+            "head_dim": w.head_dim,
+            "causal": w.causal,
+            "flop_count": flops,
+            "flop_convention": "4*N^2*d per (batch, head), halved for causal",
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": "fa_fwd_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        },
+        "parity": parity,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

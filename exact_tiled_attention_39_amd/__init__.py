@@ -1,0 +1,206 @@
+"""Python binding of libfa (exact tiled attention forward for gfx950): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of ``libfa.so``; this module converts
+torch tensors to the C-ABI's pointers, sizes and strides, allocates outputs on request, and
+raises ``FaError`` on any non-OK status. There is no fallback: if the library is not built the
+import of the binding functions raises.
+
+The C entry points (include/fa.h) are mirrored with the same names:
+``fa_fwd``, ``fa_check_args``, ``fa_status_string``, ``fa_abi_version``, ``fa_params_size``.
+``attention`` is a convenience wrapper that allocates O and LSE and calls ``fa_fwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import pathlib
+from typing import Optional, Tuple
+
+import torch  # loaded first: libfa then binds to the HIP runtime torch already loaded
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
+
+FA_F16, FA_BF16 = 0, 1
+(FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
+ FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
+FA_ABI_VERSION = 1
+
+_I64x3 = ctypes.c_int64 * 3
+
+
+class FaFwdParams(ctypes.Structure):
+    """Mirror of ``fa_fwd_params`` in include/fa.h (same field order and types)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("num_seqs", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("q_stride", _I64x3),
+        ("k_stride", _I64x3),
+        ("v_stride", _I64x3),
+        ("o_stride", _I64x3),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=ctypes.sizeof(FaFwdParams), **kw)
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfa status {status}: {message}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libfa.so once and checks that its ABI matches this binding."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = pathlib.Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"{p} is not built; run `python -m exact_tiled_attention_39_amd.build` "
+                          "(libfa has no fallback path)")
+    lib = ctypes.CDLL(str(p))
+    lib.fa_abi_version.restype = ctypes.c_int32
+    lib.fa_abi_version.argtypes = []
+    lib.fa_params_size.restype = ctypes.c_uint32
+    lib.fa_params_size.argtypes = []
+    lib.fa_check_args.restype = ctypes.c_int32
+    lib.fa_check_args.argtypes = [ctypes.POINTER(FaFwdParams)]
+    lib.fa_fwd.restype = ctypes.c_int32
+    lib.fa_fwd.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_void_p]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [ctypes.c_int32]
+    if lib.fa_abi_version() != FA_ABI_VERSION:
+        raise ImportError(f"libfa ABI {lib.fa_abi_version()} != binding ABI {FA_ABI_VERSION}")
+    if lib.fa_params_size() != ctypes.sizeof(FaFwdParams):
+        raise ImportError("fa_fwd_params layout differs between libfa and the binding")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_abi_version() -> int:
+    return int(load_library().fa_abi_version())
+
+
+def fa_params_size() -> int:
+    return int(load_library().fa_params_size())
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_check_args(params: FaFwdParams) -> int:
+    """Host-only validation of a filled FaFwdParams; returns the fa_status code."""
+    return int(load_library().fa_check_args(ctypes.byref(params)))
+
+
+_DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+
+def _strides(t: torch.Tensor):
+    s = t.stride()
+    return _I64x3(s[0], s[1], s[2])
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                lse: torch.Tensor, scale: float, causal: bool,
+                cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int]) -> FaFwdParams:
+    """Fills FaFwdParams from [B, H, N, d] tensors (strides in elements)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v and o must be 4-D [batch, heads, tokens, head_dim]")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError("q, k, v and o must share one dtype: float16 or bfloat16")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [batch, heads_q, tokens]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError(f"{name}: the head_dim dimension must be contiguous")
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if tuple(k.shape) != (b, hkv, n, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, heads_kv, tokens, head_dim] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (b, hq, n):
+        raise ValueError("o must match q and lse must be [batch, heads_q, tokens]")
+    p = FaFwdParams(
+        dtype=_DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
+        o=o.data_ptr(), lse=lse.data_ptr(), batch=b, heads_q=hq, heads_kv=hkv, seqlen=n,
+        head_dim=d, causal=int(bool(causal)), scale=float(scale),
+        q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        if cu_seqlens.device != q.device:
+            raise ValueError("cu_seqlens must live on the same device as q")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        p.cu_seqlens = cu_seqlens.data_ptr()
+        p.num_seqs = cu_seqlens.numel() - 1
+        p.max_seqlen = int(max_seqlen)
+    return p
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+           lse: torch.Tensor, *, scale: float, causal: bool = False,
+           cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueues the forward pass writing o and lse, on `stream` (default: torch's current)."""
+    lib = load_library()
+    for t in (q, k, v, o, lse):
+        if not t.is_cuda:
+            raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = int(lib.fa_fwd(ctypes.byref(p), ctypes.c_void_p(s.cuda_stream)))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+              scale: Optional[float] = None, causal: bool = False,
+              cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """softmax(scale * Q K^T) V and its per-row log-sum-exp, for [B, H, N, d] tensors.
+
+    scale defaults to 1/sqrt(d). With cu_seqlens (int32 prefix sums, batch 1) sequences are
+    packed along the token axis and attend only within themselves; max_seqlen, if omitted,
+    is read from cu_seqlens with a device-to-host copy.
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if cu_seqlens is not None and max_seqlen is None:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+        max_seqlen = int(lens.max()) if lens.numel() else 0
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+           max_seqlen=max_seqlen)
+    return o, lse
+
+
+__all__ = [
+    "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN", "FA_ERR_GQA",
+    "FA_ERR_VARLEN", "FA_ERR_ABI", "FA_ERR_LAUNCH", "FA_F16", "FA_BF16", "FaError",
+    "FaFwdParams", "attention", "fa_abi_version", "fa_check_args", "fa_fwd", "fa_params_size",
+    "fa_status_string", "load_library", "make_params",
+]

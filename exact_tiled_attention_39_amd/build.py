@@ -1,0 +1,82 @@
+"""Builds libfa.so (the HIP kernels plus the C-ABI entry points) in-tree for gfx950.
+
+Usage: python -m exact_tiled_attention_39_amd.build [--verbose]
+"""
+from __future__ import annotations
+
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIB = PKG / "libfa.so"
+
+ARCH = "gfx950"
+SOURCES = ["fa_fwd.hip", "fa_api.cpp"]
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    # packed fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; libfa needs ROCm's hipcc to build")
+    return path
+
+
+def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
+    """Compiles every source and links libfa.so next to this file (atomic replace)."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="libfa_build_") as tmp:
+        objs = []
+        procs = []
+        for src in SOURCES:
+            obj = pathlib.Path(tmp) / (src + ".o")
+            cmd = [cc, *FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+            if resource_usage and src.endswith(".hip"):
+                cmd.append("-Rpass-analysis=kernel-resource-usage")
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+            objs.append(str(obj))
+        failed = []
+        for src, proc in procs:
+            out, _ = proc.communicate()
+            text = "\n".join(l for l in out.splitlines()
+                             if "packed-fp32-ops" not in l or "error" in l.lower())
+            if text.strip() and (verbose or resource_usage or proc.returncode):
+                print(text, file=sys.stderr)
+            if proc.returncode:
+                failed.append(src)
+        if failed:
+            raise RuntimeError(f"libfa build failed for {failed}")
+        tmp_lib = pathlib.Path(tmp) / "libfa.so"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", str(tmp_lib)]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        staged = LIB.with_suffix(".so.tmp")
+        shutil.copyfile(tmp_lib, staged)
+        os.replace(staged, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="--verbose" in sys.argv, resource_usage="--resources" in sys.argv)
+    print(LIB)

@@ -1,0 +1,91 @@
+// C-ABI entry points of libfa: argument validation, status text, dispatch to the kernels.
+// The operation and the argument contract are documented in include/fa.h.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local const char* g_last_hip_error = "no HIP error recorded";
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool stride_ok(const int64_t s[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || (s[i] & 7) != 0) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+uint32_t fa_params_size(void) { return static_cast<uint32_t>(sizeof(fa_fwd_params)); }
+
+fa_status fa_check_args(const fa_fwd_params* p) {
+  if (p == nullptr) return FA_ERR_NULL;
+  if (p->struct_size != sizeof(fa_fwd_params)) return FA_ERR_ABI;
+  if (p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(p->scale)) return FA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seqlen < 0) return FA_ERR_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return FA_ERR_GQA;
+  if (p->cu_seqlens != nullptr) {
+    if (p->batch != 1 || p->num_seqs < 1) return FA_ERR_VARLEN;
+    if (p->max_seqlen < 0 || p->max_seqlen > p->seqlen) return FA_ERR_VARLEN;
+    if (p->seqlen > 0 && p->max_seqlen < 1) return FA_ERR_VARLEN;
+  }
+  if (p->seqlen == 0) return FA_OK;
+  if (!p->q || !p->k || !p->v || !p->o || !p->lse) return FA_ERR_NULL;
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
+    return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0) return FA_ERR_ALIGN;
+  if (!stride_ok(p->q_stride) || !stride_ok(p->k_stride) || !stride_ok(p->v_stride) ||
+      !stride_ok(p->o_stride))
+    return FA_ERR_ALIGN;
+  // One workgroup per (128-query tile, query head, batch entry or sequence).
+  const int64_t rows = p->cu_seqlens ? p->max_seqlen : p->seqlen;
+  const int64_t groups = p->cu_seqlens ? p->num_seqs : p->batch;
+  const int64_t grid = ((rows + 127) / 128) * int64_t(p->heads_q) * groups;
+  if (grid > INT32_MAX) return FA_ERR_SHAPE;
+  if (int64_t(p->batch) * p->heads_q * int64_t(p->seqlen) > INT64_MAX / 4) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa_status fa_fwd(const fa_fwd_params* p, void* stream) {
+  const fa_status st = fa_check_args(p);
+  if (st != FA_OK) return st;
+  if (p->seqlen == 0) return FA_OK;
+  if (p->cu_seqlens != nullptr && p->max_seqlen == 0) return FA_OK;
+  const char* err = nullptr;
+  const fa_status ls = fa::launch_forward(*p, stream, &err);
+  if (ls != FA_OK && err != nullptr) g_last_hip_error = err;
+  return ls;
+}
+
+const char* fa_status_string(int32_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype FA_F16 or FA_BF16, scale finite";
+    case FA_ERR_ALIGN:
+      return "FA_ERR_ALIGN: base pointers must be 16-byte aligned and strides non-negative "
+             "multiples of 8 elements";
+    case FA_ERR_GQA: return "FA_ERR_GQA: heads_q must be a multiple of heads_kv";
+    case FA_ERR_VARLEN:
+      return "FA_ERR_VARLEN: cu_seqlens needs batch == 1, num_seqs >= 1 and "
+             "1 <= max_seqlen <= seqlen";
+    case FA_ERR_ABI: return "FA_ERR_ABI: struct_size does not match sizeof(fa_fwd_params)";
+    case FA_ERR_LAUNCH: return g_last_hip_error;
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

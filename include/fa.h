@@ -1,0 +1,125 @@
+/*
+ * libfa -- exact tiled attention (the FlashAttention forward pass) for AMD gfx950.
+ *
+ * The operation. For every batch entry b, query head h and query token i:
+ *
+ *     s_ij   = scale * dot(Q[b, h, i, :], K[b, hk, j, :])      for every key j visible to i
+ *     O[b, h, i, :] = sum_j exp(s_ij - m_i) V[b, hk, j, :] / sum_j exp(s_ij - m_i)
+ *     LSE[b, h, i]  = m_i + ln(sum_j exp(s_ij - m_i)),           m_i = max_j s_ij
+ *
+ * with hk = h / (heads_q / heads_kv). That is softmax(scale * Q K^T) V, the self-attention of the
+ * "Flash Attention" notes (14cs17, sections "Prerequisites" and "Standard Attention Memory
+ * Analysis"), computed tile by tile with the online softmax of that page's Theorem 2 and the
+ * algorithm of its section "Flash Attention Algorithm": blocks of queries stay on chip while
+ * blocks of keys and values stream past, and neither the N x N scores S nor the probabilities
+ * P are ever written to device memory (same page, "Complexity Analysis", Theorem 3). Grouped
+ * query heads and variable sequence lengths are the FlashAttention-2 features listed in the
+ * section "Flash Attention 2 Improvements". The log-sum-exp output, the causal mask, the head
+ * grouping and the packed-sequence layout are not spelled out on the pages; the readings are:
+ *   - causal: key j is visible to query i iff j <= i (positions inside the sequence);
+ *   - grouped heads: query heads [g*r, (g+1)*r) share key/value head g, r = heads_q / heads_kv;
+ *   - packed sequences: tokens of sequence s occupy [cu_seqlens[s], cu_seqlens[s+1]) and attend
+ *     only inside that range;
+ *   - LSE is the natural logarithm of the row's sum of exp(scaled score).
+ *
+ * Arithmetic: fp16 or bf16 inputs; products and sums in fp32 on the matrix cores; the
+ * probabilities are rounded to the input type (round to nearest even) before the P V product;
+ * O is rounded to the input type (round to nearest even); LSE is fp32.
+ *
+ * Threading and memory: libfa allocates nothing and keeps no state; every call only enqueues
+ * work on the given HIP stream and returns. The caller owns every buffer.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+/* Element type of Q, K, V and O. */
+typedef enum fa_dtype {
+  FA_F16 = 0,  /* IEEE binary16 */
+  FA_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* a size is out of range, or the grid would not fit */
+  FA_ERR_UNSUPPORTED = 3, /* head_dim not 64 or 128, unknown dtype, or non-finite scale */
+  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned, or a stride is not a
+                             non-negative multiple of 8 elements */
+  FA_ERR_GQA = 5,         /* heads_q is not a multiple of heads_kv */
+  FA_ERR_VARLEN = 6,      /* cu_seqlens given with batch != 1, num_seqs < 1 or a bad max_seqlen */
+  FA_ERR_ABI = 7,         /* struct_size does not match this library's fa_fwd_params */
+  FA_ERR_LAUNCH = 8       /* the HIP launch failed (the HIP error text is kept per thread) */
+} fa_status;
+
+/*
+ * Arguments of one forward call. All pointers are device pointers except the struct itself.
+ *
+ * Layout: q is [batch, heads_q, seqlen, head_dim]; k and v are [batch, heads_kv, seqlen,
+ * head_dim]; o is [batch, heads_q, seqlen, head_dim]. The last (head_dim) dimension is
+ * contiguous; the other three are given by the *_stride arrays, in elements, in the order
+ * (batch, head, token). lse is a contiguous fp32 array [batch, heads_q, seqlen].
+ *
+ * Packed variable-length sequences: pass cu_seqlens (device, int32, num_seqs + 1 non-decreasing
+ * prefix sums with cu_seqlens[0] == 0 and cu_seqlens[num_seqs] == seqlen), batch == 1, and
+ * max_seqlen >= every sequence length (it sizes the grid). Zero-length sequences are allowed.
+ * libfa never reads device memory on the host, so it cannot check the cu_seqlens contents:
+ * they are the caller's promise. Without cu_seqlens, num_seqs and max_seqlen are ignored.
+ */
+typedef struct fa_fwd_params {
+  uint32_t struct_size;   /* must equal sizeof(fa_fwd_params) (see fa_params_size) */
+  int32_t dtype;          /* fa_dtype */
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;                /* written in full for every valid token */
+  float* lse;             /* written in full for every valid token */
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t seqlen;         /* tokens per batch entry; total packed tokens with cu_seqlens */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t causal;         /* non-zero: key j visible to query i iff j <= i */
+  float scale;            /* any finite value; 1/sqrt(head_dim) is the usual choice */
+  int32_t num_seqs;
+  int32_t max_seqlen;
+  const int32_t* cu_seqlens; /* NULL for fixed-length batches */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} fa_fwd_params;
+
+/* FA_ABI_VERSION of the built library. */
+int32_t fa_abi_version(void);
+
+/* sizeof(fa_fwd_params) as compiled into the library. */
+uint32_t fa_params_size(void);
+
+/* Host-only argument validation (no device call): the checks fa_fwd performs first. */
+fa_status fa_check_args(const fa_fwd_params* p);
+
+/*
+ * Enqueue the forward pass on `stream` (a hipStream_t; NULL means the default stream).
+ * Returns FA_OK once the kernel is enqueued; argument errors are returned before any device
+ * call. seqlen == 0 is a no-op returning FA_OK. Faults inside the kernel surface at the
+ * caller's next synchronisation of the stream. NaN or Inf inputs are not checked and propagate.
+ */
+fa_status fa_fwd(const fa_fwd_params* p, void* stream);
+
+/* Static text for a status code; for FA_ERR_LAUNCH, the HIP error of this thread's last
+ * failed launch. Never NULL. */
+const char* fa_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

@@ -1,0 +1,131 @@
+"""The C-ABI boundary on the host: the library loads, exports what include/fa.h declares, and
+validates arguments before any device call (CPU only, no kernel is launched)."""
+import ctypes
+import pathlib
+import re
+import subprocess
+
+import pytest
+import torch
+
+import exact_tiled_attention_39_amd as fa
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "fa.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_abi_version", "fa_check_args", "fa_fwd",
+                                    "fa_params_size", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(fa.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert set(declared_functions()) <= exported
+
+
+def test_abi_version_and_struct_layout():
+    assert fa.fa_abi_version() == fa.FA_ABI_VERSION
+    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 192
+    assert fa.FaFwdParams.cu_seqlens.offset == 88
+    assert fa.FaFwdParams.o_stride.offset == 168
+
+
+ALIGNED = 0x10000
+
+
+def good(**kw):
+    base = dict(dtype=fa.FA_BF16, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4,
+                lse=ALIGNED * 5, batch=2, heads_q=8, heads_kv=2, seqlen=100, head_dim=128,
+                causal=1, scale=0.125)
+    strides = dict(q_stride=(8 * 100 * 128, 100 * 128, 128), k_stride=(2 * 100 * 128, 100 * 128, 128),
+                   v_stride=(2 * 100 * 128, 100 * 128, 128), o_stride=(8 * 100 * 128, 100 * 128, 128))
+    base.update(kw)
+    p = fa.FaFwdParams(**{k: v for k, v in base.items() if not k.endswith("_stride")})
+    for name, val in strides.items():
+        setattr(p, name, fa._I64x3(*kw.get(name, val)))
+    return p
+
+
+def test_valid_arguments_pass():
+    assert fa.fa_check_args(good()) == fa.FA_OK
+    assert fa.fa_check_args(good(head_dim=64, dtype=fa.FA_F16, heads_kv=8, causal=0)) == fa.FA_OK
+    assert fa.fa_check_args(good(scale=0.0)) == fa.FA_OK
+    assert fa.fa_check_args(good(scale=-3.0)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL),
+    (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_UNSUPPORTED),
+    (dict(batch=0), fa.FA_ERR_SHAPE),
+    (dict(heads_q=0), fa.FA_ERR_SHAPE),
+    (dict(seqlen=-1), fa.FA_ERR_SHAPE),
+    (dict(heads_kv=3), fa.FA_ERR_GQA),
+    (dict(q=ALIGNED + 8), fa.FA_ERR_ALIGN),
+    (dict(o=ALIGNED + 2), fa.FA_ERR_ALIGN),
+    (dict(lse=ALIGNED + 2), fa.FA_ERR_ALIGN),
+    (dict(k_stride=(0, 0, 132)), fa.FA_ERR_ALIGN),
+    (dict(v_stride=(-128, 0, 128)), fa.FA_ERR_ALIGN),
+    (dict(cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=50), fa.FA_ERR_VARLEN),  # batch 2
+    (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=0, max_seqlen=50), fa.FA_ERR_VARLEN),
+    (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=101), fa.FA_ERR_VARLEN),
+    (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=0), fa.FA_ERR_VARLEN),
+    (dict(batch=2 ** 20, heads_q=2 ** 10, heads_kv=2 ** 10, seqlen=2 ** 20), fa.FA_ERR_SHAPE),
+])
+def test_each_error_is_reported_before_any_device_call(kw, status):
+    p = good(**kw)
+    assert fa.fa_check_args(p) == status
+    lib = fa.load_library()
+    assert lib.fa_fwd(ctypes.byref(p), None) == status  # rejected before touching a device
+
+
+def test_struct_size_mismatch_and_null_params():
+    p = good()
+    p.struct_size = 100
+    assert fa.fa_check_args(p) == fa.FA_ERR_ABI
+    lib = fa.load_library()
+    assert lib.fa_check_args(None) == fa.FA_ERR_NULL
+    assert lib.fa_fwd(None, None) == fa.FA_ERR_NULL
+
+
+def test_empty_problem_is_a_no_op():
+    p = good(seqlen=0, q=0, k=0, v=0, o=0, lse=0)
+    lib = fa.load_library()
+    assert lib.fa_fwd(ctypes.byref(p), None) == fa.FA_OK
+
+
+def test_status_strings():
+    for s in range(9):
+        text = fa.fa_status_string(s)
+        assert text and (s == fa.FA_ERR_LAUNCH or text.startswith("FA_"))
+    assert fa.fa_status_string(1234) == "unknown fa_status"
+
+
+def test_binding_rejects_host_tensors_and_bad_layouts():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q, q.clone(), torch.zeros(1, 2, 8), scale=0.1)
+    with pytest.raises(ValueError):
+        fa.make_params(q, q, q, q, torch.zeros(1, 2, 8), 0.1, False, None, None).dtype  # fp32 lse ok
+        fa.make_params(q, q.float(), q, q, torch.zeros(1, 2, 8), 0.1, False, None, None)
+    with pytest.raises(ValueError):
+        fa.make_params(q, q, q, q, torch.zeros(1, 2, 8), 0.1, False,
+                       torch.zeros(3, dtype=torch.int64), 4)
+    p = fa.make_params(q, q, q, q.clone(), torch.zeros(1, 2, 8), 0.1, True, None, None)
+    assert (p.batch, p.heads_q, p.heads_kv, p.seqlen, p.head_dim, p.causal) == (1, 2, 2, 8, 64, 1)
+    assert list(p.q_stride) == [1024, 512, 64]
+    assert fa.fa_check_args(p) == fa.FA_OK
