@@ -13,9 +13,13 @@ thread_local const char* g_last_hip_error = "no HIP error recorded";
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-bool stride_ok(const int64_t s[3]) {
+// Strides are element counts for (batch, head, token). All must be non-negative multiples of
+// 8 (16-byte rows); token rows may not overlap, and a token stride is at most 2^23 elements so
+// that the byte extent of one 64-row K/V tile fits a 32-bit buffer range.
+bool stride_ok(const int64_t s[3], int32_t head_dim, int32_t seqlen) {
   for (int i = 0; i < 3; ++i)
     if (s[i] < 0 || (s[i] & 7) != 0) return false;
+  if (seqlen > 1 && (s[2] < head_dim || s[2] > (int64_t(1) << 23))) return false;
   return true;
 }
 
@@ -45,10 +49,12 @@ fa_status fa_check_args(const fa_fwd_params* p) {
   if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
     return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0) return FA_ERR_ALIGN;
-  if (!stride_ok(p->q_stride) || !stride_ok(p->k_stride) || !stride_ok(p->v_stride) ||
-      !stride_ok(p->o_stride))
+  if (!stride_ok(p->q_stride, p->head_dim, p->seqlen) ||
+      !stride_ok(p->k_stride, p->head_dim, p->seqlen) ||
+      !stride_ok(p->v_stride, p->head_dim, p->seqlen) ||
+      !stride_ok(p->o_stride, p->head_dim, p->seqlen))
     return FA_ERR_ALIGN;
-  // One workgroup per (128-query tile, query head, batch entry or sequence).
+  // At most one workgroup per (128 query rows, query head, batch entry or sequence).
   const int64_t rows = p->cu_seqlens ? p->max_seqlen : p->seqlen;
   const int64_t groups = p->cu_seqlens ? p->num_seqs : p->batch;
   const int64_t grid = ((rows + 127) / 128) * int64_t(p->heads_q) * groups;
@@ -76,8 +82,8 @@ const char* fa_status_string(int32_t status) {
     case FA_ERR_UNSUPPORTED:
       return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype FA_F16 or FA_BF16, scale finite";
     case FA_ERR_ALIGN:
-      return "FA_ERR_ALIGN: base pointers must be 16-byte aligned and strides non-negative "
-             "multiples of 8 elements";
+      return "FA_ERR_ALIGN: base pointers must be 16-byte aligned, strides non-negative "
+             "multiples of 8 elements, token strides in [head_dim, 2^23]";
     case FA_ERR_GQA: return "FA_ERR_GQA: heads_q must be a multiple of heads_kv";
     case FA_ERR_VARLEN:
       return "FA_ERR_VARLEN: cu_seqlens needs batch == 1, num_seqs >= 1 and "

@@ -19,8 +19,12 @@
 //    of O^T += V^T P^T; the matching V^T operand comes from row-major V tiles in LDS through
 //    the gfx950 transposing read ds_read_b64_tr_b16, with the key order permuted to match the
 //    accumulator layout (keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step for half-wave h).
-//  * K and V tiles of 64 keys are double-buffered in LDS. Rows are 16-byte-chunk XOR swizzled
-//    so that both the 128-bit K reads and the transposing V reads spread over the banks.
+//  * K and V tiles of 64 keys are double-buffered in LDS, filled from buffer loads whose
+//    out-of-range part reads as zero (ragged tails need no branches). Rows are padded so both
+//    the 128-bit K reads and the transposing V reads are free of bank conflicts, and every LDS
+//    address in the loop is a per-lane base plus an immediate.
+//  * The reference maximum of the online softmax is raised lazily (only when a tile's maximum
+//    exceeds it by more than 2^8), so the rescale of O is rare after the first tiles.
 //  * exp is exp2 with scale * log2(e) folded into one FMA per score.
 //  * Causal blocks stop at the diagonal; only diagonal and ragged-tail tiles are masked; a
 //    wave whose rows are all above a tile skips that tile.
@@ -30,6 +34,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -50,9 +55,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
-constexpr int kBlockM = 128;  // query rows per workgroup (B_r)
+constexpr int kBlockM = 256;  // query rows per workgroup (B_r): 8 waves x 32 rows
 constexpr int kBlockN = 64;   // keys per K/V tile (B_c)
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 struct KernelArgs {
   const uint16_t* q;
@@ -108,37 +113,55 @@ struct Elem<false> {
   }
 };
 
-// Physical 16-byte chunk of logical chunk `ch` in LDS row `row`.
+// LDS tile geometry. Rows are padded instead of swizzled so that every LDS address in the
+// loop is a per-lane base plus a compile-time immediate:
+//  * K rows are read as 16-byte chunks by 32 consecutive rows (the MFMA A operand); a skew of
+//    16 bytes per row puts 16 consecutive rows in 16 distinct 16-byte bank groups;
+//  * V rows are read by the transposing read, 4 consecutive rows x 64 bytes per 32 lanes; a
+//    skew of 64 bytes per row spreads those 4 rows over all four 64-byte bank groups.
 template <int D>
-__device__ __forceinline__ int swizzle(int row, int ch) {
-  if constexpr (D == 128) {
-    return ch ^ (((row & 3) << 2) | ((row >> 2) & 3));
-  } else {
-    return ch ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-  }
+struct Tile {
+  static constexpr int kPitchK = D + 8;    // elements
+  static constexpr int kPitchV = D + 32;   // elements
+  static constexpr int kBytesK = kBlockN * kPitchK * 2;
+  static constexpr int kBytesV = kBlockN * kPitchV * 2;
+  static constexpr int kLdsBytes = 2 * (kBytesK + kBytesV);  // two stages of K and V
+};
+
+// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int D>
-__device__ __forceinline__ int lds_offset(int row, int col) {  // in elements
-  return row * D + (swizzle<D>(row, col >> 3) << 3) + (col & 7);
-}
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// Running maxima grow lazily: O and l are rescaled only when some row's tile maximum exceeds
+// the reference maximum by more than this many powers of two. Any reference maximum gives the
+// same O = O~ / l and LSE = m + log2(l); this bound keeps exp2(s - m) <= 2^8.
+constexpr float kLazyRescale = 8.0f;
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const KernelArgs p) {
   using E = Elem<BF16>;
-  constexpr int kChunks = D / 8;                       // 16-byte chunks per row
-  constexpr int kSteps = D / 16;                       // k-steps of the S^T product
-  constexpr int kOBlocks = D / 32;                     // 32-wide head-dim blocks of O^T
-  constexpr int kLoads = kBlockN * kChunks / kThreads; // 16-byte loads per thread per tensor
-  constexpr int kTile = kBlockN * D;                   // elements per K (or V) tile
+  using T = Tile<D>;
+  constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+  constexpr int kSteps = D / 16;                        // k-steps of the S^T product
+  constexpr int kOBlocks = D / 32;                      // 32-wide head-dim blocks of O^T
+  constexpr int kGroupThreads = kThreads / 2;           // one wave group stages one tensor
+  constexpr int kLoads = kBlockN * kChunks / kGroupThreads;  // 16-byte loads per thread
+  constexpr int kRowsPerPass = kGroupThreads / kChunks;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * kTile];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[T::kLdsBytes];
+  unsigned char* lds_k = smem;                     // stage s at s * kBytesK
+  unsigned char* lds_v = smem + 2 * T::kBytesK;    // stage s at s * kBytesV
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int grp = wave >> 2;   // wave group: 0 stages K tiles, 1 stages V tiles
   const int half = lane >> 5;  // which 8-element half of each 16-wide k step this lane feeds
   const int lq = lane & 31;    // query column owned by this lane
 
@@ -180,8 +203,10 @@ void fa_fwd_kernel(const KernelArgs p) {
   const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
 
   // ---- Q^T fragments (B operand), resident for the whole kernel -----------------------
-  const int wrow0 = q0 + wave * 32;  // first query row of this wave
-  const int qrow = wrow0 + lq;       // query row of this lane
+  // The two waves sharing a SIMD (w and w + 4) take neighbouring 32-row slices, so both
+  // groups reach the causal diagonal at nearly the same tile.
+  const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
+  const int qrow = wrow0 + lq;                          // query row of this lane
   u32x4 qf[kSteps];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
@@ -193,72 +218,102 @@ void fa_fwd_kernel(const KernelArgs p) {
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS (swizzled) ------------------------
-  u32x4 kr[kLoads], vr[kLoads];
-  auto load_tile = [&](int tile) {
+  // ---- K/V staging: group 0 stages K tiles, group 1 stages V tiles ----------------------
+  // buffer loads (zero past the sequence end) -> registers -> LDS (padded rows)
+  const int gt = tid & (kGroupThreads - 1);
+  const int ld_row = gt / kChunks;
+  const int ld_ch = gt % kChunks;
+  const uint16_t* ld_base = grp ? vbase : kbase;
+  const int64_t ld_sn = grp ? p.v_sn : p.k_sn;
+  int ld_voff[kLoads];
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int id = r * kThreads + tid;
-      const int row = id / kChunks, ch = id % kChunks;
-      const int key = tile * kBlockN + row;
-      if (key < slen) {
-        kr[r] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * p.k_sn + ch * 8);
-        vr[r] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * p.v_sn + ch * 8);
-      } else {
-        kr[r] = u32x4{0, 0, 0, 0};  // zero rows: masked scores, and no NaN from stale V
-        vr[r] = u32x4{0, 0, 0, 0};
-      }
-    }
+  for (int r = 0; r < kLoads; ++r)
+    ld_voff[r] = int((ld_row + r * kRowsPerPass) * ld_sn * 2) + ld_ch * 16;
+  unsigned char* st_base = grp ? lds_v + ld_row * T::kPitchV * 2 + ld_ch * 16
+                               : lds_k + ld_row * T::kPitchK * 2 + ld_ch * 16;
+  const int st_pass = (grp ? T::kPitchV : T::kPitchK) * 2 * kRowsPerPass;
+  const int st_stage = grp ? T::kBytesV : T::kBytesK;
+
+  u32x4 stg[kLoads];
+  // issue the loads of tile `tile` of this group's tensor
+  auto gload = [&](int tile) __attribute__((always_inline)) {
+    const int key0 = tile * kBlockN;
+    const int rows = min(slen - key0, kBlockN);  // rows of this tile inside the sequence
+    const int bytes = int((rows - 1) * ld_sn * 2) + D * 2;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ld_base + int64_t(key0) * ld_sn, bytes);
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r)
+      stg[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_voff[r], 0, 0);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * 2 * kTile;
-    uint16_t* vs = ks + kTile;
+  // write the staged tile into its LDS stage
+  auto lds_put = [&](int tile) __attribute__((always_inline)) {
+    unsigned char* dst = st_base + (tile & 1) * st_stage;
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-      const int id = r * kThreads + tid;
-      const int row = id / kChunks, ch = id % kChunks;
-      const int off = row * D + (swizzle<D>(row, ch) << 3);
-      *reinterpret_cast<u32x4*>(ks + off) = kr[r];
-      *reinterpret_cast<u32x4*>(vs + off) = vr[r];
-    }
+    for (int r = 0; r < kLoads; ++r) *reinterpret_cast<u32x4*>(dst + r * st_pass) = stg[r];
   };
 
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units (Theorem 2's m)
+  // Per-lane LDS read bases; everything else in the M phase is an immediate offset.
+  //  K (A operand of S^T): row lq of each 32-key half, 16-byte chunk (2s + half).
+  const unsigned char* rd_k = lds_k + lq * T::kPitchK * 2 + half * 16;
+  //  V (transposing read): the 16 lanes of a group cover 4 consecutive keys x 16 head-dims.
+  const int sub = lane & 15;
+  const unsigned char* rd_v = lds_v + (4 * half + (sub >> 2)) * T::kPitchV * 2 +
+                              (16 * ((lane >> 4) & 1) + 4 * (sub & 3)) * 2;
+
+  float m_run = -INFINITY;  // reference maximum of scaled scores, log2 units (Theorem 2's m)
   float l_run = 0.f;        // running sum of this half-wave's keys (Theorem 2's l)
   f32x16 oacc[kOBlocks];    // unnormalised O^T: lane holds head-dims of its query column
 #pragma unroll
   for (int j = 0; j < kOBlocks; ++j) oacc[j] = f32x16{};
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    const bool has_next = tile + 1 < n_tiles;
-    if (has_next) load_tile(tile + 1);  // in flight while this tile is consumed
-
-    const int key0 = tile * kBlockN;
-    const bool wave_live = wrow0 < slen && !(CAUSAL && key0 > wrow0 + 31);
-    if (wave_live) {
-      const uint16_t* ks = smem + buf * 2 * kTile;
-      const uint16_t* vs = ks + kTile;
-
-      // S^T = K Q^T for two 32-key halves of the tile.
-      f32x16 sacc[2];
+  f32x16 sacc[2];           // S^T of the tile between its M and V phases
+  u32x4 pb[2][2];           // P^T of the previous tile, in the input type (B operands)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const int row = kb * 32 + lq;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(ks + lds_offset<D>(row, s * 16 + half * 8));
-          sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
-        }
-      }
+    for (int tt = 0; tt < 2; ++tt) pb[kb][tt] = u32x4{0, 0, 0, 0};
 
-      // Mask keys past the sequence end, and above the diagonal when causal.
+  // S^T = K Q^T, two 32-key halves (A: K rows from LDS stage KS).
+  auto s_mfma = [&](auto ks, int kb, int s) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks)::value;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(rd_k + KS * T::kBytesK +
+                                                   kb * 32 * T::kPitchK * 2 + s * 32);
+    sacc[kb] = E::mfma(a, qf[s], s == 0 ? f32x16{} : sacc[kb]);
+  };
+  // O^T += V^T P^T for head-dim block j, key half kb, 16-key step tt (V from stage VS).
+  // The 16 lanes of a group receive head-dim column (lane % 32) of four consecutive keys per
+  // transposing read; keys {16t+4h+0..3, 16t+8+4h+0..3} form the 8-element k slice of
+  // half-wave h, matching the accumulator rows of P^T.
+  auto pv_mfma = [&](auto vs, int j, int kb, int tt) __attribute__((always_inline)) {
+    constexpr int VS = decltype(vs)::value;
+    const unsigned char* base =
+        rd_v + VS * T::kBytesV + (kb * 32 + 16 * tt) * T::kPitchV * 2 + j * 64;
+    const u32x2 lo = E::read_tr(reinterpret_cast<const uint16_t*>(base));
+    const u32x2 hi = E::read_tr(reinterpret_cast<const uint16_t*>(base + 8 * T::kPitchV * 2));
+    oacc[j] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kb][tt], oacc[j]);
+  };
+
+  // M phase (matrix cores), straight-line: S of tile p from K stage KS, and P V of tile p - 1
+  // from V stage 1 - KS. Before the first tile P is zero and V stage 1 holds zeros; after the
+  // last tile the S result is never used.
+  auto phase_m = [&](auto ks) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks)::value;
+    constexpr int kS = 2 * kSteps;     // S MFMAs per tile
+    constexpr int kPv = 4 * kOBlocks;  // PV MFMAs per tile
+    __builtin_amdgcn_s_setprio(1);  // the wave feeding the matrix cores issues first
+#pragma unroll
+    for (int i = 0; i < (kS > kPv ? kS : kPv); ++i) {
+      if (i < kS) s_mfma(Int<KS>{}, i / kSteps, i % kSteps);
+      if (i < kPv) pv_mfma(Int<1 - KS>{}, i / 4, (i / 2) & 1, i & 1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // V phase (vector units): online softmax of S_p (Theorem 2) into P_p, plus this group's
+  // share of the K/V staging: write tile p + 1 into LDS, start loading tile p + 2.
+  // Keys this wave cannot see (past the sequence end, above the diagonal) get P = 0.
+  auto phase_v = [&](int tile) __attribute__((always_inline)) {
+    if (tile >= 0 && tile < n_tiles) {
+      const int key0 = tile * kBlockN;
       const bool edge = (key0 + kBlockN > slen) || (CAUSAL && key0 + kBlockN - 1 > wrow0);
       if (edge) {
 #pragma unroll
@@ -271,19 +326,20 @@ void fa_fwd_kernel(const KernelArgs p) {
           }
         }
       }
-
-      // Online softmax (Theorem 2): new running max, rescale factor, exponentials.
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * p.c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      const float neg_m = -m_use;
+      if (__builtin_amdgcn_ballot_w64(mx * p.c > m_run + kLazyRescale)) {
+        const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * p.c);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
+      }
+      const float neg_m = -m_run;
       float rsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -293,13 +349,8 @@ void fa_fwd_kernel(const KernelArgs p) {
           sacc[kb][i] = e;
           rsum += e;
         }
-      l_run = l_run * alpha + rsum;
-#pragma unroll
-      for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
-
-      // P^T fragments in the input type: B operand of step t of key half kb is
-      // accumulator entries 8t .. 8t+7.
-      u32x4 pb[2][2];
+      l_run += rsum;
+      // B operand of step tt of key half kb is accumulator entries 8tt .. 8tt+7.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -307,30 +358,66 @@ void fa_fwd_kernel(const KernelArgs p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             pb[kb][tt][e] = E::pack(sacc[kb][8 * tt + 2 * e], sacc[kb][8 * tt + 2 * e + 1]);
+    }
+    if (tile + 1 < n_tiles) lds_put(tile + 1);
+    if (tile + 2 < n_tiles) gload(tile + 2);
+  };
 
-      // O^T += V^T P^T. Lane reads 4 head-dim columns x 4 keys per transposing read; the
-      // 16 lanes of a group together receive column (lane % 32) of 4 consecutive keys.
-      const int sub = lane & 15;
-      const int col_in = 16 * ((lane >> 4) & 1) + 4 * (sub & 3);
-#pragma unroll
-      for (int j = 0; j < kOBlocks; ++j) {
-        const int col = j * 32 + col_in;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int r0 = kb * 32 + 16 * tt + 4 * half + (sub >> 2);
-            const u32x2 lo = E::read_tr(vs + lds_offset<D>(r0, col));
-            const u32x2 hi = E::read_tr(vs + lds_offset<D>(r0 + 8, col));
-            const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            oacc[j] = E::mfma(a, pb[kb][tt], oacc[j]);
-          }
-        }
+  // Phase boundary: a workgroup barrier that the instruction scheduler may not move
+  // register-only work across (a plain barrier orders memory operations only).
+  auto phase_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- ping-pong schedule --------------------------------------------------------------
+  // Slot 2p:   group 0 runs M(p),   group 1 runs V(p - 1)
+  // Slot 2p+1: group 0 runs V(p),   group 1 runs M(p)
+  // so on every SIMD one wave feeds the matrix cores while the other runs the softmax.
+  // K_p is read in slots 2p and 2p+1 (stage p & 1) and written by group 0 in slot 2p - 1;
+  // V_p is read in slots 2p+2 and 2p+3 (stage p & 1) and written by group 1 in slot 2p.
+  // Both groups execute 2 (n_tiles + 1) barriers after the prologue's one.
+  {
+    // stage 1 of K and V starts as zeros (it is read before it is first written)
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    for (int off = tid * 16; off < T::kBytesK; off += kThreads * 16)
+      *reinterpret_cast<u32x4*>(lds_k + T::kBytesK + off) = zero;
+    for (int off = tid * 16; off < T::kBytesV; off += kThreads * 16)
+      *reinterpret_cast<u32x4*>(lds_v + T::kBytesV + off) = zero;
+  }
+  gload(0);
+  if (grp == 0) {
+    lds_put(0);
+    if (n_tiles > 1) gload(1);
+  }
+  __syncthreads();
+  if (grp == 0) {
+    for (int tile = 0; tile <= n_tiles; tile += 2) {
+      phase_m(Int<0>{});
+      phase_sync();
+      phase_v(tile);
+      phase_sync();
+      if (tile + 1 <= n_tiles) {
+        phase_m(Int<1>{});
+        phase_sync();
+        phase_v(tile + 1);
+        phase_sync();
       }
     }
-
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+  } else {
+    for (int tile = 0; tile <= n_tiles; tile += 2) {
+      phase_v(tile - 1);
+      phase_sync();
+      phase_m(Int<0>{});
+      phase_sync();
+      if (tile + 1 <= n_tiles) {
+        phase_v(tile);
+        phase_sync();
+        phase_m(Int<1>{});
+        phase_sync();
+      }
+    }
   }
 
   // ---- epilogue: O = O~ / l, LSE = ln(l) + m; both half-waves hold partial sums --------

@@ -51,8 +51,9 @@ typedef enum fa_status {
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,       /* a size is out of range, or the grid would not fit */
   FA_ERR_UNSUPPORTED = 3, /* head_dim not 64 or 128, unknown dtype, or non-finite scale */
-  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned, or a stride is not a
-                             non-negative multiple of 8 elements */
+  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned, a stride is not a
+                             non-negative multiple of 8 elements, or a token stride is below
+                             head_dim (overlapping rows) or above 2^23 elements */
   FA_ERR_GQA = 5,         /* heads_q is not a multiple of heads_kv */
   FA_ERR_VARLEN = 6,      /* cu_seqlens given with batch != 1, num_seqs < 1 or a bad max_seqlen */
   FA_ERR_ABI = 7,         /* struct_size does not match this library's fa_fwd_params */

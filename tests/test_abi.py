@@ -80,6 +80,8 @@ def test_valid_arguments_pass():
     (dict(lse=ALIGNED + 2), fa.FA_ERR_ALIGN),
     (dict(k_stride=(0, 0, 132)), fa.FA_ERR_ALIGN),
     (dict(v_stride=(-128, 0, 128)), fa.FA_ERR_ALIGN),
+    (dict(q_stride=(0, 0, 64)), fa.FA_ERR_ALIGN),          # overlapping token rows
+    (dict(o_stride=(0, 0, 2 ** 23 + 8)), fa.FA_ERR_ALIGN),  # token stride too large
     (dict(cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=50), fa.FA_ERR_VARLEN),  # batch 2
     (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=0, max_seqlen=50), fa.FA_ERR_VARLEN),
     (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=101), fa.FA_ERR_VARLEN),
