@@ -96,6 +96,20 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
     }
 
 
+def copy_calibration(torch, mib: int) -> int:
+    """A plain copy of a known number of bytes: its FETCH_SIZE / WRITE_SIZE readings per launch
+    against mib * 2^20 give the factor that turns those counters into bytes."""
+    n = mib * 2 ** 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +118,9 @@ def main() -> int:
     ap.add_argument("--workload", default=si.HEADLINE, choices=si.WORKLOAD_ORDER)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 launches), the "
+                         "known-size reference that scales the HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -114,6 +131,10 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration_mib:
+        return copy_calibration(torch, args.copy_calibration_mib)
+
     import exact_tiled_attention_39_amd as fa
 
     fa.load_library()

@@ -22,7 +22,7 @@ SOURCES = ["fa_fwd.hip", "fa_api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     # packed fp32 VALU forms are kept out of the device code

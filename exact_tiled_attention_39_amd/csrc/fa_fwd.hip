@@ -7,27 +7,32 @@
 // Theorem 2, write O_i), with FlashAttention-2's choices from the section "Flash Attention 2
 // Improvements": the grid runs over query blocks, and O is normalised by l once at the end.
 //
-// Mapping onto the hardware (one workgroup = one 128-row query block of one head):
-//  * 4 waves of 64 lanes; wave w owns query rows [32w, 32w + 32) of the block, so waves never
-//    reduce across each other.
+// Mapping onto the hardware (one workgroup = one 256-row query block of one head):
+//  * 8 waves of 64 lanes in two groups of four; wave w owns 32 query rows of the block, so
+//    waves never reduce across each other.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{bf16,f16}: the
 //    A operand is 32 keys x 16 head-dims read from LDS, the B operand is Q^T held in VGPRs for
 //    the whole kernel. In the 32x32 accumulator lane L holds query column L % 32 and 16 keys,
-//    so the row maximum and row sum are in-lane plus one exchange between the two half-waves,
-//    and the rescale of O by exp2(m_old - m_new) is a per-lane multiply.
+//    so row statistics are in-lane plus one exchange between the two half-waves, and the
+//    rescale of O by exp2(m_old - m_new) is a per-lane multiply.
 //  * The exponentiated scores, rounded to the input type, are used directly as the B operand
-//    of O^T += V^T P^T; the matching V^T operand comes from row-major V tiles in LDS through
-//    the gfx950 transposing read ds_read_b64_tr_b16, with the key order permuted to match the
-//    accumulator layout (keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step for half-wave h).
-//  * K and V tiles of 64 keys are double-buffered in LDS, filled from buffer loads whose
-//    out-of-range part reads as zero (ragged tails need no branches). Rows are padded so both
-//    the 128-bit K reads and the transposing V reads are free of bank conflicts, and every LDS
-//    address in the loop is a per-lane base plus an immediate.
-//  * The reference maximum of the online softmax is raised lazily (only when a tile's maximum
-//    exceeds it by more than 2^8), so the rescale of O is rare after the first tiles.
+//    of O^T += V^T P^T; the matching V^T operand comes from V through the gfx950 transposing
+//    read ds_read_b64_tr_b16, with the key order permuted to match the accumulator layout
+//    (keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key step for half-wave h).
+//  * Ping-pong: the two wave groups alternate, one barrier-delimited phase apart, between an
+//    M phase (the S MFMAs of tile p and the P V MFMAs of tile p - 1) and a V phase (the online
+//    softmax of tile p), so each SIMD overlaps one wave's softmax with the other's matrix work.
+//  * K and V tiles of 64 keys stream into four-stage LDS rings by direct-to-LDS buffer loads
+//    (no staging registers, no LDS store instructions), issued two to three tiles ahead.
+//    Each tile is stored fragment-major: every 1 KB block holds exactly one MFMA operand in
+//    lane order, so every LDS read in the loop is contiguous (free of bank conflicts) and is a
+//    per-lane base plus an immediate. Out-of-range rows read as zero (ragged tails).
+//  * Running maxima are raised lazily: a tile is exponentiated against the current reference
+//    maximum and only if some lane's sum exceeds 2^15 (a score that far above the reference,
+//    or the first tile) is the tile maximum formed and O, l rescaled. Any reference maximum
+//    gives the same O = O~ / l and LSE = m + log2(l); the bound keeps each exp2 <= 2^15.
 //  * exp is exp2 with scale * log2(e) folded into one FMA per score.
-//  * Causal blocks stop at the diagonal; only diagonal and ragged-tail tiles are masked; a
-//    wave whose rows are all above a tile skips that tile.
+//  * Causal blocks stop at the diagonal; only diagonal and ragged-tail tiles are masked.
 //  * The workgroup index is remapped so that the blocks of one head run on one XCD (its L2
 //    serves the K/V re-reads), heaviest causal blocks first.
 #include <hip/hip_runtime.h>
@@ -35,6 +40,7 @@
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -58,6 +64,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlockM = 256;  // query rows per workgroup (B_r): 8 waves x 32 rows
 constexpr int kBlockN = 64;   // keys per K/V tile (B_c)
 constexpr int kThreads = 512;
+constexpr int kStages = 4;    // depth of the K and V rings in LDS
 
 struct KernelArgs {
   const uint16_t* q;
@@ -89,7 +96,7 @@ struct Elem<true> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* lds) {
+  static __device__ __forceinline__ u32x2 read_tr(const unsigned char* lds) {
     bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(lds));
     return __builtin_bit_cast(u32x2, r);
   }
@@ -104,7 +111,7 @@ struct Elem<false> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ u32x2 read_tr(const uint16_t* lds) {
+  static __device__ __forceinline__ u32x2 read_tr(const unsigned char* lds) {
     f16x4_tr r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_PTR(f16x4_tr))(lds));
     return __builtin_bit_cast(u32x2, r);
   }
@@ -113,55 +120,86 @@ struct Elem<false> {
   }
 };
 
-// LDS tile geometry. Rows are padded instead of swizzled so that every LDS address in the
-// loop is a per-lane base plus a compile-time immediate:
-//  * K rows are read as 16-byte chunks by 32 consecutive rows (the MFMA A operand); a skew of
-//    16 bytes per row puts 16 consecutive rows in 16 distinct 16-byte bank groups;
-//  * V rows are read by the transposing read, 4 consecutive rows x 64 bytes per 32 lanes; a
-//    skew of 64 bytes per row spreads those 4 rows over all four 64-byte bank groups.
+// Fragment-major tile geometry. A K tile is kKBlocks blocks of 1 KB, block (kb, s) holding
+// the A operand of the S^T MFMA for key half kb and k-step s in lane order (lane L: 16 bytes
+// of key row 32 kb + L % 32, head-dims 16 s + 8 (L / 32) .. + 7). A V tile is kVBlocks blocks,
+// block (kb, tt, j) holding the two transposing reads of the P V MFMA for key half kb, 16-key
+// step tt and head-dim block j: bytes [0, 512) serve keys 16 tt + 0..7 of the half, bytes
+// [512, 1024) keys 16 tt + 8..15, 8 bytes per lane in lane order.
 template <int D>
-struct Tile {
-  static constexpr int kPitchK = D + 8;    // elements
-  static constexpr int kPitchV = D + 32;   // elements
-  static constexpr int kBytesK = kBlockN * kPitchK * 2;
-  static constexpr int kBytesV = kBlockN * kPitchV * 2;
-  static constexpr int kLdsBytes = 2 * (kBytesK + kBytesV);  // two stages of K and V
+struct Geo {
+  static constexpr int kSteps = D / 16;            // k-steps of the S^T product
+  static constexpr int kOBlocks = D / 32;          // 32-wide head-dim blocks of O^T
+  static constexpr int kKBlocks = 2 * kSteps;      // blocks per K tile
+  static constexpr int kVBlocks = 4 * kOBlocks;    // blocks per V tile
+  static constexpr int kKBytes = kKBlocks * 1024;  // = 64 keys x D x 2 bytes
+  static constexpr int kVBytes = kVBlocks * 1024;
+  static constexpr int kDmaPerWave = kKBlocks / 4;  // 1 KB loads per staging wave per tile
+  static constexpr int kLdsBytes = kStages * (kKBytes + kVBytes);
+  static_assert(kKBlocks == kVBlocks, "K and V tiles have the same size");
 };
 
-// Raw buffer resource over [base, base + bytes): loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+// Raw buffer descriptor over [base, base + bytes) in scalar registers: loads past the end
+// return zeros. (base and bytes are wave-uniform.)
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  r[1] = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane(uint32_t(bytes));
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane L's 16 bytes at byte offset voff of the
+// buffer land at LDS byte lds_addr + 16 L. Written as one asm statement so that the compiler's
+// memory-counter bookkeeping does not treat every later LDS read as dependent on it; the
+// kernel waits for these loads explicitly (wait_vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// s_waitcnt on outstanding vector-memory operations only (lgkm and exp counters left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-// Running maxima grow lazily: O and l are rescaled only when some row's tile maximum exceeds
-// the reference maximum by more than this many powers of two. Any reference maximum gives the
-// same O = O~ / l and LSE = m + log2(l); this bound keeps exp2(s - m) <= 2^8.
-constexpr float kLazyRescale = 8.0f;
+// A tile is rescaled (its maximum formed) only when some lane's sum of exp2 exceeds this.
+constexpr float kLazyBound = 32768.0f;
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const KernelArgs p) {
   using E = Elem<BF16>;
-  using T = Tile<D>;
-  constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-  constexpr int kSteps = D / 16;                        // k-steps of the S^T product
-  constexpr int kOBlocks = D / 32;                      // 32-wide head-dim blocks of O^T
-  constexpr int kGroupThreads = kThreads / 2;           // one wave group stages one tensor
-  constexpr int kLoads = kBlockN * kChunks / kGroupThreads;  // 16-byte loads per thread
-  constexpr int kRowsPerPass = kGroupThreads / kChunks;
+  using G = Geo<D>;
+  constexpr int kSteps = G::kSteps;
+  constexpr int kOBlocks = G::kOBlocks;
+  constexpr int kDma = G::kDmaPerWave;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[T::kLdsBytes];
-  unsigned char* lds_k = smem;                     // stage s at s * kBytesK
-  unsigned char* lds_v = smem + 2 * T::kBytesK;    // stage s at s * kBytesV
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::kLdsBytes];
+  unsigned char* const lds_k = smem;                          // stage s at s * kKBytes
+  unsigned char* const lds_v = smem + kStages * G::kKBytes;   // stage s at s * kVBytes
+  // LDS byte address of smem (the value M0 takes for a direct-to-LDS load into it)
+  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_PTR(unsigned char))(smem))));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2;   // wave group: 0 stages K tiles, 1 stages V tiles
+  const int gw = wave & 3;     // wave within its group
   const int half = lane >> 5;  // which 8-element half of each 16-wide k step this lane feeds
   const int lq = lane & 31;    // query column owned by this lane
 
@@ -205,60 +243,76 @@ void fa_fwd_kernel(const KernelArgs p) {
   // ---- Q^T fragments (B operand), resident for the whole kernel -----------------------
   // The two waves sharing a SIMD (w and w + 4) take neighbouring 32-row slices, so both
   // groups reach the causal diagonal at nearly the same tile.
-  const int wrow0 = q0 + 32 * (2 * (wave & 3) + grp);  // first query row of this wave
-  const int qrow = wrow0 + lq;                          // query row of this lane
+  const int wrow0 = q0 + 32 * (2 * gw + grp);  // first query row of this wave
+  const int qrow = wrow0 + lq;                  // query row of this lane
+  // buffer loads over this wave's valid rows: rows past the sequence end read as zero
   u32x4 qf[kSteps];
+  {
+    const int rows = min(max(slen - wrow0, 0), 32);
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(qb + int64_t(wrow0) * p.q_sn), (short)0,
+        rows > 0 ? int((rows - 1) * p.q_sn * 2) + D * 2 : 0, 0x00020000);
+    const int qoff = int(lq * p.q_sn * 2) + half * 16;
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    if (qrow < slen) {
-      qf[s] = *reinterpret_cast<const u32x4*>(qb + int64_t(qrow) * p.q_sn + s * 16 + half * 8);
-      qf[s] = (qf[s] & p.q_and) ^ p.q_xor;
-    } else {
-      qf[s] = u32x4{0, 0, 0, 0};
-    }
+    for (int s = 0; s < kSteps; ++s)
+      qf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + s * 32,
+                                                                              0, 0));
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) qf[s] = (qf[s] & p.q_and) ^ p.q_xor;
   }
 
-  // ---- K/V staging: group 0 stages K tiles, group 1 stages V tiles ----------------------
-  // buffer loads (zero past the sequence end) -> registers -> LDS (padded rows)
-  const int gt = tid & (kGroupThreads - 1);
-  const int ld_row = gt / kChunks;
-  const int ld_ch = gt % kChunks;
+  // ---- direct-to-LDS staging: group 0 streams K tiles, group 1 streams V tiles ----------
+  // Staging wave gw fills blocks [gw * kDma, (gw + 1) * kDma) of each tile; lane L of a load
+  // writes bytes [16 L, 16 L + 16) of its block, so it fetches the 16 source bytes that the
+  // fragment-major layout puts there.
   const uint16_t* ld_base = grp ? vbase : kbase;
   const int64_t ld_sn = grp ? p.v_sn : p.k_sn;
-  int ld_voff[kLoads];
+  int ld_voff[kDma];
 #pragma unroll
-  for (int r = 0; r < kLoads; ++r)
-    ld_voff[r] = int((ld_row + r * kRowsPerPass) * ld_sn * 2) + ld_ch * 16;
-  unsigned char* st_base = grp ? lds_v + ld_row * T::kPitchV * 2 + ld_ch * 16
-                               : lds_k + ld_row * T::kPitchK * 2 + ld_ch * 16;
-  const int st_pass = (grp ? T::kPitchV : T::kPitchK) * 2 * kRowsPerPass;
-  const int st_stage = grp ? T::kBytesV : T::kBytesK;
-
-  u32x4 stg[kLoads];
-  // issue the loads of tile `tile` of this group's tensor
-  auto gload = [&](int tile) __attribute__((always_inline)) {
+  for (int i = 0; i < kDma; ++i) {
+    const int blk = gw * kDma + i;
+    int row, col;
+    if (grp == 0) {
+      // K block (kb, s): key 32 kb + L % 32, head-dims 16 s + 8 (L / 32) .. + 7
+      const int kb = blk / kSteps, s = blk % kSteps;
+      row = 32 * kb + (lane & 31);
+      col = 16 * s + 8 * (lane >> 5);
+    } else {
+      // V block (kb, tt, j): lanes 2m, 2m + 1 of the transposing read of keys part * 8 .. + 7
+      const int kbtt = blk / kOBlocks, j = blk % kOBlocks;
+      const int part = lane >> 5;
+      const int m = 2 * (lane & 31);
+      row = 16 * kbtt + 8 * part + 4 * (m >> 5) + ((m & 15) >> 2);
+      col = 32 * j + 16 * ((m >> 4) & 1) + 4 * (m & 3);
+    }
+    ld_voff[i] = int(row * ld_sn * 2) + col * 2;
+  }
+  // issue the loads of tile `tile` into ring stage ST of this group's tensor
+  auto dma = [&](auto st, int tile) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
     const int key0 = tile * kBlockN;
     const int rows = min(slen - key0, kBlockN);  // rows of this tile inside the sequence
     const int bytes = int((rows - 1) * ld_sn * 2) + D * 2;
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(ld_base + int64_t(key0) * ld_sn, bytes);
+    const u32x4 rsrc = make_rsrc(ld_base + int64_t(key0) * ld_sn, bytes);
+    const uint32_t dst = lds_ring + (grp ? kStages * G::kKBytes + ST * G::kVBytes
+                                         : ST * G::kKBytes) + gw * kDma * 1024;
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r)
-      stg[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_voff[r], 0, 0);
+    for (int i = 0; i < kDma; ++i) dma16(rsrc, dst + i * 1024, ld_voff[i]);
   };
-  // write the staged tile into its LDS stage
-  auto lds_put = [&](int tile) __attribute__((always_inline)) {
-    unsigned char* dst = st_base + (tile & 1) * st_stage;
-#pragma unroll
-    for (int r = 0; r < kLoads; ++r) *reinterpret_cast<u32x4*>(dst + r * st_pass) = stg[r];
+  // wait until the loads of the tile issued `after` tiles before the most recent are in LDS
+  // (after = number of this wave's tiles issued later, 0..2)
+  auto dma_wait = [&](int after) __attribute__((always_inline)) {
+    if (after >= 2)
+      wait_vmcnt<2 * kDma>();
+    else if (after == 1)
+      wait_vmcnt<kDma>();
+    else
+      wait_vmcnt<0>();
   };
 
   // Per-lane LDS read bases; everything else in the M phase is an immediate offset.
-  //  K (A operand of S^T): row lq of each 32-key half, 16-byte chunk (2s + half).
-  const unsigned char* rd_k = lds_k + lq * T::kPitchK * 2 + half * 16;
-  //  V (transposing read): the 16 lanes of a group cover 4 consecutive keys x 16 head-dims.
-  const int sub = lane & 15;
-  const unsigned char* rd_v = lds_v + (4 * half + (sub >> 2)) * T::kPitchV * 2 +
-                              (16 * ((lane >> 4) & 1) + 4 * (sub & 3)) * 2;
+  const unsigned char* rd_k = lds_k + lane * 16;
+  const unsigned char* rd_v = lds_v + lane * 8;
 
   float m_run = -INFINITY;  // reference maximum of scaled scores, log2 units (Theorem 2's m)
   float l_run = 0.f;        // running sum of this half-wave's keys (Theorem 2's l)
@@ -272,151 +326,187 @@ void fa_fwd_kernel(const KernelArgs p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) pb[kb][tt] = u32x4{0, 0, 0, 0};
 
-  // S^T = K Q^T, two 32-key halves (A: K rows from LDS stage KS).
-  auto s_mfma = [&](auto ks, int kb, int s) __attribute__((always_inline)) {
-    constexpr int KS = decltype(ks)::value;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(rd_k + KS * T::kBytesK +
-                                                   kb * 32 * T::kPitchK * 2 + s * 32);
-    sacc[kb] = E::mfma(a, qf[s], s == 0 ? f32x16{} : sacc[kb]);
-  };
-  // O^T += V^T P^T for head-dim block j, key half kb, 16-key step tt (V from stage VS).
-  // The 16 lanes of a group receive head-dim column (lane % 32) of four consecutive keys per
-  // transposing read; keys {16t+4h+0..3, 16t+8+4h+0..3} form the 8-element k slice of
-  // half-wave h, matching the accumulator rows of P^T.
-  auto pv_mfma = [&](auto vs, int j, int kb, int tt) __attribute__((always_inline)) {
-    constexpr int VS = decltype(vs)::value;
-    const unsigned char* base =
-        rd_v + VS * T::kBytesV + (kb * 32 + 16 * tt) * T::kPitchV * 2 + j * 64;
-    const u32x2 lo = E::read_tr(reinterpret_cast<const uint16_t*>(base));
-    const u32x2 hi = E::read_tr(reinterpret_cast<const uint16_t*>(base + 8 * T::kPitchV * 2));
-    oacc[j] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kb][tt], oacc[j]);
-  };
-
   // M phase (matrix cores), straight-line: S of tile p from K stage KS, and P V of tile p - 1
-  // from V stage 1 - KS. Before the first tile P is zero and V stage 1 holds zeros; after the
+  // from V stage VS. Before the first tile P is zero and the V stage holds zeros; after the
   // last tile the S result is never used.
-  auto phase_m = [&](auto ks) __attribute__((always_inline)) {
+  // The 2 kSteps S MFMAs and 4 kOBlocks P V MFMAs alternate (n even: S, n odd: P V), ordered
+  // so that consecutive MFMAs into one accumulator are at least four apart. The LDS operand
+  // of MFMA n + kAhead is read before MFMA n issues, and each step is pinned in place, so the
+  // read latency hides behind kAhead matrix operations.
+  constexpr int kMfma = 2 * (2 * kSteps);
+  static_assert(2 * kSteps == 4 * kOBlocks, "S and P V MFMAs pair up");
+  constexpr int kAhead = 8;
+  auto phase_m = [&](auto ks, auto vs) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks)::value;
-    constexpr int kS = 2 * kSteps;     // S MFMAs per tile
-    constexpr int kPv = 4 * kOBlocks;  // PV MFMAs per tile
+    constexpr int VS = decltype(vs)::value;
+    u32x4 opnd[kMfma];
+    auto fetch = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value;
+      if constexpr ((n & 1) == 0) {
+        constexpr int kb = (n >> 1) & 1, s = n >> 2;  // S(kb, s)
+        opnd[n] = *reinterpret_cast<const u32x4*>(rd_k + KS * G::kKBytes +
+                                                  (kb * kSteps + s) * 1024);
+      } else {
+        constexpr int i = n >> 1, j = i % kOBlocks, kbtt = i / kOBlocks;  // PV(j, kb, tt)
+        const unsigned char* base = rd_v + VS * G::kVBytes + (kbtt * kOBlocks + j) * 1024;
+        const u32x2 lo = E::read_tr(base);
+        const u32x2 hi = E::read_tr(base + 512);
+        opnd[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+    auto issue = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value;
+      if constexpr ((n & 1) == 0) {
+        constexpr int kb = (n >> 1) & 1, s = n >> 2;
+        sacc[kb] = E::mfma(opnd[n], qf[s], s == 0 ? f32x16{} : sacc[kb]);
+      } else {
+        constexpr int i = n >> 1, j = i % kOBlocks, kbtt = i / kOBlocks;
+        oacc[j] = E::mfma(opnd[n], pb[kbtt >> 1][kbtt & 1], oacc[j]);
+      }
+    };
     __builtin_amdgcn_s_setprio(1);  // the wave feeding the matrix cores issues first
-#pragma unroll
-    for (int i = 0; i < (kS > kPv ? kS : kPv); ++i) {
-      if (i < kS) s_mfma(Int<KS>{}, i / kSteps, i % kSteps);
-      if (i < kPv) pv_mfma(Int<1 - KS>{}, i / 4, (i / 2) & 1, i & 1);
-    }
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      (fetch(Int<n>{}), ...);
+    }(std::make_integer_sequence<int, kAhead>{});
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      ((
+           [&] {
+             if constexpr (n + kAhead < kMfma) fetch(Int<n + kAhead>{});
+             issue(Int<n>{});
+             __builtin_amdgcn_sched_barrier(0);
+           }()),
+       ...);
+    }(std::make_integer_sequence<int, kMfma>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // V phase (vector units): online softmax of S_p (Theorem 2) into P_p, plus this group's
-  // share of the K/V staging: write tile p + 1 into LDS, start loading tile p + 2.
-  // Keys this wave cannot see (past the sequence end, above the diagonal) get P = 0.
-  auto phase_v = [&](int tile) __attribute__((always_inline)) {
-    if (tile >= 0 && tile < n_tiles) {
-      const int key0 = tile * kBlockN;
-      const bool edge = (key0 + kBlockN > slen) || (CAUSAL && key0 + kBlockN - 1 > wrow0);
-      if (edge) {
+  // Online softmax of S_tile (Theorem 2) into P_tile. Keys this wave cannot see (past the
+  // sequence end, above the diagonal) get P = 0.
+  auto softmax = [&](int tile) __attribute__((always_inline)) {
+    const int key0 = tile * kBlockN;
+    const bool edge = (key0 + kBlockN > slen) || (CAUSAL && key0 + kBlockN - 1 > wrow0);
+    if (edge) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool ok = key < slen && (!CAUSAL || key <= qrow);
-            sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool ok = key < slen && (!CAUSAL || key <= qrow);
+          sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
         }
       }
+    }
+    f32x16 ex[2];
+    float part[4];
+    auto expo = [&]() __attribute__((always_inline)) {
+      const float neg_m = -m_run;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ex[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], p.c, neg_m));
+          part[i & 3] += ex[kb][i];
+        }
+    };
+    expo();
+    float rsum = (part[0] + part[1]) + (part[2] + part[3]);
+    // Rare path: the first tile (no reference yet), or a score far above the reference.
+    // NaN sums also land here; they propagate to the output either way.
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= kLazyBound))) {
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      if (__builtin_amdgcn_ballot_w64(mx * p.c > m_run + kLazyRescale)) {
-        const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * p.c);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-        m_run = m_new;
-        l_run *= alpha;
+      const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * p.c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
-      }
-      const float neg_m = -m_run;
-      float rsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], p.c, neg_m));
-          sacc[kb][i] = e;
-          rsum += e;
-        }
-      l_run += rsum;
-      // B operand of step tt of key half kb is accumulator entries 8tt .. 8tt+7.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pb[kb][tt][e] = E::pack(sacc[kb][8 * tt + 2 * e], sacc[kb][8 * tt + 2 * e + 1]);
+      for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
+      expo();
+      rsum = (part[0] + part[1]) + (part[2] + part[3]);
     }
-    if (tile + 1 < n_tiles) lds_put(tile + 1);
-    if (tile + 2 < n_tiles) gload(tile + 2);
+    l_run += rsum;
+    // B operand of step tt of key half kb is accumulator entries 8tt .. 8tt+7.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pb[kb][tt][e] = E::pack(ex[kb][8 * tt + 2 * e], ex[kb][8 * tt + 2 * e + 1]);
   };
 
-  // Phase boundary: a workgroup barrier that the instruction scheduler may not move
-  // register-only work across (a plain barrier orders memory operations only).
+  // Phase boundary: this wave's LDS reads are complete, then a workgroup barrier that the
+  // instruction scheduler may not move register-only work across.
   auto phase_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- ping-pong schedule --------------------------------------------------------------
+  // ---- ping-pong schedule over ring stages ---------------------------------------------
   // Slot 2p:   group 0 runs M(p),   group 1 runs V(p - 1)
   // Slot 2p+1: group 0 runs V(p),   group 1 runs M(p)
-  // so on every SIMD one wave feeds the matrix cores while the other runs the softmax.
-  // K_p is read in slots 2p and 2p+1 (stage p & 1) and written by group 0 in slot 2p - 1;
-  // V_p is read in slots 2p+2 and 2p+3 (stage p & 1) and written by group 1 in slot 2p.
+  // M(p) reads K_p (stage p % 4) and V_{p-1} (stage (p - 1) % 4).
+  // K_p is read in slots 2p, 2p + 1; group 0 issues K_{p+3} in slot 2p + 1 and has waited
+  // for K_{p+1} before that slot's closing barrier.
+  // V_p is read in slots 2p + 2, 2p + 3; group 1 issues V_{p+2} in slot 2p and has waited
+  // for V_p before the closing barrier of slot 2p + 1.
   // Both groups execute 2 (n_tiles + 1) barriers after the prologue's one.
   {
-    // stage 1 of K and V starts as zeros (it is read before it is first written)
+    // V stage 3 is read (with P = 0) before any tile lands there: it must hold finite data.
     const u32x4 zero = u32x4{0, 0, 0, 0};
-    for (int off = tid * 16; off < T::kBytesK; off += kThreads * 16)
-      *reinterpret_cast<u32x4*>(lds_k + T::kBytesK + off) = zero;
-    for (int off = tid * 16; off < T::kBytesV; off += kThreads * 16)
-      *reinterpret_cast<u32x4*>(lds_v + T::kBytesV + off) = zero;
+    for (int off = tid * 16; off < G::kVBytes; off += kThreads * 16)
+      *reinterpret_cast<u32x4*>(lds_v + 3 * G::kVBytes + off) = zero;
   }
-  gload(0);
   if (grp == 0) {
-    lds_put(0);
-    if (n_tiles > 1) gload(1);
+    dma(Int<0>{}, 0);
+    if (n_tiles > 1) dma(Int<1>{}, 1);
+    if (n_tiles > 2) dma(Int<2>{}, 2);
+    dma_wait(min(n_tiles - 1, 2));  // K_0 in LDS
+  } else {
+    dma(Int<0>{}, 0);
+    if (n_tiles > 1) dma(Int<1>{}, 1);
   }
   __syncthreads();
+
+  // one ring step of each group; ST = p % 4
+  auto step_g0 = [&](auto st, int tile) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
+    phase_sync();
+    if (tile < n_tiles) softmax(tile);
+    if (tile + 3 < n_tiles) dma(Int<(ST + 3) & 3>{}, tile + 3);
+    if (tile + 1 < n_tiles) dma_wait(min(n_tiles - 2 - tile, 2));  // K_{tile+1} in LDS
+    phase_sync();
+  };
+  auto step_g1 = [&](auto st, int tile) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st)::value;
+    if (tile >= 1) softmax(tile - 1);
+    if (tile + 2 < n_tiles) dma(Int<(ST + 2) & 3>{}, tile + 2);
+    phase_sync();
+    phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
+    if (tile < n_tiles) dma_wait(min(n_tiles - 1 - tile, 2));  // V_tile in LDS
+    phase_sync();
+  };
   if (grp == 0) {
-    for (int tile = 0; tile <= n_tiles; tile += 2) {
-      phase_m(Int<0>{});
-      phase_sync();
-      phase_v(tile);
-      phase_sync();
-      if (tile + 1 <= n_tiles) {
-        phase_m(Int<1>{});
-        phase_sync();
-        phase_v(tile + 1);
-        phase_sync();
-      }
+    for (int tile = 0; tile <= n_tiles; tile += 4) {
+      step_g0(Int<0>{}, tile);
+      if (tile + 1 <= n_tiles) step_g0(Int<1>{}, tile + 1);
+      if (tile + 2 <= n_tiles) step_g0(Int<2>{}, tile + 2);
+      if (tile + 3 <= n_tiles) step_g0(Int<3>{}, tile + 3);
     }
   } else {
-    for (int tile = 0; tile <= n_tiles; tile += 2) {
-      phase_v(tile - 1);
-      phase_sync();
-      phase_m(Int<0>{});
-      phase_sync();
-      if (tile + 1 <= n_tiles) {
-        phase_v(tile);
-        phase_sync();
-        phase_m(Int<1>{});
-        phase_sync();
-      }
+    for (int tile = 0; tile <= n_tiles; tile += 4) {
+      step_g1(Int<0>{}, tile);
+      if (tile + 1 <= n_tiles) step_g1(Int<1>{}, tile + 1);
+      if (tile + 2 <= n_tiles) step_g1(Int<2>{}, tile + 2);
+      if (tile + 3 <= n_tiles) step_g1(Int<3>{}, tile + 3);
     }
   }
 
