@@ -84,7 +84,7 @@ struct KernelArgs {
   float c;            // |scale| * log2(e), or log2(e) when scale == 0
   uint32_t q_and;     // 0 when scale == 0 (all scores are exactly 0), else all ones
   uint32_t q_xor;     // 0x80008000 when scale < 0: Q is negated exactly and c stays positive
-  int32_t xcd_group;  // 1: keep the blocks of a head on one XCD
+  int32_t xcd_group;  // 1: keep the blocks of a (batch, head) pair on one XCD
 };
 
 template <bool BF16>
@@ -204,21 +204,21 @@ void fa_fwd_kernel(const KernelArgs p) {
   const int lq = lane & 31;    // query column owned by this lane
 
   // ---- work item: (query block, head, batch entry / sequence) -------------------------
-  const int total = gridDim.x;
-  int item = blockIdx.x;
-  if (p.xcd_group && (total & 7) == 0) {
-    // Workgroups are dealt to the 8 XCDs round-robin; give XCD x a contiguous range.
-    item = (item & 7) * (total >> 3) + (item >> 3);
-  }
+  // Blocks are taken heaviest first (causal blocks near the end of the sequence see the most
+  // keys), so the tail of the launch is made of the lightest blocks. With xcd_group the
+  // (batch, head) pairs are split evenly over the 8 XCDs, to which workgroups are dealt
+  // round-robin, so that the K/V re-reads of a head (and of the query heads that share it)
+  // stay in one XCD's L2; within an XCD the order is again heaviest first.
+  const int pairs = gridDim.x / p.n_qblocks;
   int bh, t;
-  if (VARLEN) {
-    // Heaviest blocks first across all sequences and heads (lengths differ per sequence).
-    const int pairs = total / p.n_qblocks;
-    t = item / pairs;
-    bh = item - t * pairs;
+  if (p.xcd_group && (pairs & 7) == 0) {
+    const int per = pairs >> 3;
+    const int r = blockIdx.x >> 3;
+    t = r / per;
+    bh = (blockIdx.x & 7) * per + (r - t * per);
   } else {
-    bh = item / p.n_qblocks;
-    t = item - bh * p.n_qblocks;
+    t = blockIdx.x / pairs;
+    bh = blockIdx.x - t * pairs;
   }
   const int qblock = CAUSAL ? (p.n_qblocks - 1 - t) : t;
   const int b = bh / p.heads_q;
