@@ -22,6 +22,7 @@
 //  * Ping-pong: the two wave groups alternate, one barrier-delimited phase apart, between an
 //    M phase (the S MFMAs of tile p and the P V MFMAs of tile p - 1) and a V phase (the online
 //    softmax of tile p), so each SIMD overlaps one wave's softmax with the other's matrix work.
+//    The softmax wave runs at the higher issue priority: its exp2 chain is the longer phase.
 //  * K and V tiles of 64 keys stream into four-stage LDS rings by direct-to-LDS buffer loads
 //    (no staging registers, no LDS store instructions), issued two to three tiles ahead.
 //    Each tile is stored fragment-major: every 1 KB block holds exactly one MFMA operand in
@@ -33,6 +34,7 @@
 //    gives the same O = O~ / l and LSE = m + log2(l); the bound keeps each exp2 <= 2^15.
 //  * exp is exp2 with scale * log2(e) folded into one FMA per score.
 //  * Causal blocks stop at the diagonal; only diagonal and ragged-tail tiles are masked.
+//    Causal blocks are aligned to the sequence end, so a partial block is the cheapest one.
 //  * The workgroup index is remapped so that the blocks of one head run on one XCD (its L2
 //    serves the K/V re-reads), heaviest causal blocks first.
 #include <hip/hip_runtime.h>
@@ -84,7 +86,8 @@ struct KernelArgs {
   float c;            // |scale| * log2(e), or log2(e) when scale == 0
   uint32_t q_and;     // 0 when scale == 0 (all scores are exactly 0), else all ones
   uint32_t q_xor;     // 0x80008000 when scale < 0: Q is negated exactly and c stays positive
-  int32_t xcd_group;  // 1: keep the blocks of a (batch, head) pair on one XCD
+  int32_t xcd_group;  // 0: plain order; 1: (batch, head) pairs in 8 contiguous runs, one per
+                      // XCD; 2: kv heads dealt to the 8 XCDs in turn (heads_kv % 8 == 0)
 };
 
 template <bool BF16>
@@ -203,33 +206,51 @@ void fa_fwd_kernel(const KernelArgs p) {
   const int half = lane >> 5;  // which 8-element half of each 16-wide k step this lane feeds
   const int lq = lane & 31;    // query column owned by this lane
 
-  // ---- work item: (query block, head, batch entry / sequence) -------------------------
-  // Blocks are taken heaviest first (causal blocks near the end of the sequence see the most
-  // keys), so the tail of the launch is made of the lightest blocks. With xcd_group the
-  // (batch, head) pairs are split evenly over the 8 XCDs, to which workgroups are dealt
-  // round-robin, so that the K/V re-reads of a head (and of the query heads that share it)
-  // stay in one XCD's L2; within an XCD the order is again heaviest first.
+  // ---- work item: (query block t, head, batch entry / sequence) -----------------------
+  // Workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8). With xcd_group the
+  // blocks of one (batch, head) pair, and of the query heads sharing its kv head, all land on
+  // one XCD, whose L2 then serves their K/V re-reads; mode 2 gives every XCD an equal share of
+  // the heads of every batch entry, which also balances sequences of unequal length. Within
+  // an XCD, t runs 0, 1, ... over query blocks n_qblocks - 1 - t, heaviest causal block
+  // first, so the tail of the launch is made of the lightest blocks.
   const int pairs = gridDim.x / p.n_qblocks;
-  int bh, t;
-  if (p.xcd_group && (pairs & 7) == 0) {
-    const int per = pairs >> 3;
+  int t, b, h;
+  if (p.xcd_group == 2) {
+    const int per = pairs >> 3;      // (batch, head) pairs per XCD
+    const int hpx = p.heads_q >> 3;  // query heads per XCD per batch entry
     const int r = blockIdx.x >> 3;
     t = r / per;
-    bh = (blockIdx.x & 7) * per + (r - t * per);
+    const int j = r - t * per;
+    b = j / hpx;
+    const int hh = j - b * hpx;
+    const int kvl = hh / p.group, gq = hh - kvl * p.group;
+    h = ((kvl << 3) + int(blockIdx.x & 7)) * p.group + gq;
   } else {
-    t = blockIdx.x / pairs;
-    bh = blockIdx.x - t * pairs;
+    int bh;
+    if (p.xcd_group == 1 && (pairs & 7) == 0) {
+      const int per = pairs >> 3;
+      const int r = blockIdx.x >> 3;
+      t = r / per;
+      bh = (blockIdx.x & 7) * per + (r - t * per);
+    } else {
+      t = blockIdx.x / pairs;
+      bh = blockIdx.x - t * pairs;
+    }
+    b = bh / p.heads_q;
+    h = bh - b * p.heads_q;
   }
-  const int qblock = CAUSAL ? (p.n_qblocks - 1 - t) : t;
-  const int b = bh / p.heads_q;
-  const int h = bh - b * p.heads_q;
   int seq0 = 0, slen = p.seqlen, bidx = b;
   if (VARLEN) {
     seq0 = p.cu_seqlens[b];
     slen = p.cu_seqlens[b + 1] - seq0;
     bidx = 0;
   }
-  const int q0 = qblock * kBlockM;
+  // Causal blocks are aligned to the sequence end (shifted down by pad rows), so a partial
+  // block is block 0, which sees the fewest keys (its rows below 0 are idle); block u then
+  // sees 4 u + ceil((256 - pad) / 64) key tiles, and the order stays heaviest first.
+  const int qblock = CAUSAL ? (p.n_qblocks - 1 - t) : t;
+  const int pad = CAUSAL ? (-slen) & (kBlockM - 1) : 0;
+  const int q0 = kBlockM * qblock - pad;
   if (q0 >= slen) return;  // uniform across the workgroup, before any barrier
   const int hk = h / p.group;
 
@@ -237,7 +258,7 @@ void fa_fwd_kernel(const KernelArgs p) {
   const uint16_t* kbase = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
   const uint16_t* vbase = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
 
-  const int kv_end = CAUSAL ? min(slen, q0 + kBlockM) : slen;
+  const int kv_end = CAUSAL ? q0 + kBlockM : slen;
   const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
 
   // ---- Q^T fragments (B operand), resident for the whole kernel -----------------------
@@ -245,14 +266,16 @@ void fa_fwd_kernel(const KernelArgs p) {
   // groups reach the causal diagonal at nearly the same tile.
   const int wrow0 = q0 + 32 * (2 * gw + grp);  // first query row of this wave
   const int qrow = wrow0 + lq;                  // query row of this lane
-  // buffer loads over this wave's valid rows: rows past the sequence end read as zero
+  // buffer loads over this wave's rows inside [0, slen): rows outside read as zero
   u32x4 qf[kSteps];
   {
-    const int rows = min(max(slen - wrow0, 0), 32);
+    const int lo = max(wrow0, 0);
+    const int rows = max(min(slen, wrow0 + 32) - lo, 0);
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(qb + int64_t(wrow0) * p.q_sn), (short)0,
+        const_cast<uint16_t*>(qb + int64_t(lo) * p.q_sn), (short)0,
         rows > 0 ? int((rows - 1) * p.q_sn * 2) + D * 2 : 0, 0x00020000);
-    const int qoff = int(lq * p.q_sn * 2) + half * 16;
+    // a lane below row 0 reads far past the end of the range
+    const int qoff = qrow >= 0 ? int((qrow - lo) * p.q_sn * 2) + half * 16 : 0x40000000;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
       qf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + s * 32,
@@ -329,25 +352,33 @@ void fa_fwd_kernel(const KernelArgs p) {
   // M phase (matrix cores), straight-line: S of tile p from K stage KS, and P V of tile p - 1
   // from V stage VS. Before the first tile P is zero and the V stage holds zeros; after the
   // last tile the S result is never used.
-  // The 2 kSteps S MFMAs and 4 kOBlocks P V MFMAs alternate (n even: S, n odd: P V), ordered
-  // so that consecutive MFMAs into one accumulator are at least four apart. The LDS operand
-  // of MFMA n + kAhead is read before MFMA n issues, and each step is pinned in place, so the
-  // read latency hides behind kAhead matrix operations.
+  // The 2 kSteps S MFMAs and 4 kOBlocks P V MFMAs go in groups of eight: four S MFMAs (k-steps
+  // 2g and 2g + 1 of both key halves, so each Q^T operand feeds two in a row) then four P V
+  // MFMAs (P V index 4g .. 4g + 3, which for d = 128 share one P^T operand). Consecutive MFMAs
+  // into one accumulator are at least two apart. The LDS operand of MFMA n + kAhead is read
+  // before MFMA n issues, and each step is pinned in place, so the read latency hides behind
+  // kAhead matrix operations.
   constexpr int kMfma = 2 * (2 * kSteps);
   static_assert(2 * kSteps == 4 * kOBlocks, "S and P V MFMAs pair up");
+  static_assert(kMfma % 8 == 0, "groups of four S and four P V MFMAs");
   constexpr int kAhead = 8;
+  // MFMA n of the phase: an S MFMA (index 2 s + kb) or a P V MFMA (index i, head-dim block
+  // i % kOBlocks, 16-key step i / kOBlocks)
+  constexpr auto is_s = [](int n) constexpr { return (n & 7) < 4; };
+  constexpr auto s_idx = [](int n) constexpr { return 4 * (n >> 3) + (n & 7); };
+  constexpr auto pv_idx = [](int n) constexpr { return 4 * (n >> 3) + (n & 7) - 4; };
   auto phase_m = [&](auto ks, auto vs) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks)::value;
     constexpr int VS = decltype(vs)::value;
     u32x4 opnd[kMfma];
     auto fetch = [&](auto nn) __attribute__((always_inline)) {
       constexpr int n = decltype(nn)::value;
-      if constexpr ((n & 1) == 0) {
-        constexpr int kb = (n >> 1) & 1, s = n >> 2;  // S(kb, s)
+      if constexpr (is_s(n)) {
+        constexpr int kb = s_idx(n) & 1, s = s_idx(n) >> 1;  // S(kb, s)
         opnd[n] = *reinterpret_cast<const u32x4*>(rd_k + KS * G::kKBytes +
                                                   (kb * kSteps + s) * 1024);
       } else {
-        constexpr int i = n >> 1, j = i % kOBlocks, kbtt = i / kOBlocks;  // PV(j, kb, tt)
+        constexpr int i = pv_idx(n), j = i % kOBlocks, kbtt = i / kOBlocks;  // PV(j, kb, tt)
         const unsigned char* base = rd_v + VS * G::kVBytes + (kbtt * kOBlocks + j) * 1024;
         const u32x2 lo = E::read_tr(base);
         const u32x2 hi = E::read_tr(base + 512);
@@ -356,15 +387,14 @@ void fa_fwd_kernel(const KernelArgs p) {
     };
     auto issue = [&](auto nn) __attribute__((always_inline)) {
       constexpr int n = decltype(nn)::value;
-      if constexpr ((n & 1) == 0) {
-        constexpr int kb = (n >> 1) & 1, s = n >> 2;
+      if constexpr (is_s(n)) {
+        constexpr int kb = s_idx(n) & 1, s = s_idx(n) >> 1;
         sacc[kb] = E::mfma(opnd[n], qf[s], s == 0 ? f32x16{} : sacc[kb]);
       } else {
-        constexpr int i = n >> 1, j = i % kOBlocks, kbtt = i / kOBlocks;
+        constexpr int i = pv_idx(n), j = i % kOBlocks, kbtt = i / kOBlocks;
         oacc[j] = E::mfma(opnd[n], pb[kbtt >> 1][kbtt & 1], oacc[j]);
       }
     };
-    __builtin_amdgcn_s_setprio(1);  // the wave feeding the matrix cores issues first
     [&]<int... n>(std::integer_sequence<int, n...>) {
       (fetch(Int<n>{}), ...);
     }(std::make_integer_sequence<int, kAhead>{});
@@ -377,22 +407,25 @@ void fa_fwd_kernel(const KernelArgs p) {
            }()),
        ...);
     }(std::make_integer_sequence<int, kMfma>{});
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of S_tile (Theorem 2) into P_tile. Keys this wave cannot see (past the
   // sequence end, above the diagonal) get P = 0.
+  // The softmax wave issues ahead of the matrix wave on its SIMD: the V phase, not the MFMA
+  // chain, is the longer of the two.
   auto softmax = [&](int tile) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
     const int key0 = tile * kBlockN;
     const bool edge = (key0 + kBlockN > slen) || (CAUSAL && key0 + kBlockN - 1 > wrow0);
     if (edge) {
+      // entry i of key half kb is key key0 + off + 4 half; it is visible while off <= lim
+      const int lim = (CAUSAL ? min(slen - 1, qrow) : slen - 1) - key0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool ok = key < slen && (!CAUSAL || key <= qrow);
-          sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+          const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+          sacc[kb][i] = off <= lim ? sacc[kb][i] : -INFINITY;
         }
       }
     }
@@ -401,13 +434,14 @@ void fa_fwd_kernel(const KernelArgs p) {
     auto expo = [&]() __attribute__((always_inline)) {
       const float neg_m = -m_run;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[r] = 0.f;
-#pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           ex[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], p.c, neg_m));
-          part[i & 3] += ex[kb][i];
+          if (kb == 0 && i < 4)
+            part[i] = ex[kb][i];
+          else
+            part[i & 3] += ex[kb][i];
         }
     };
     expo();
@@ -438,6 +472,7 @@ void fa_fwd_kernel(const KernelArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pb[kb][tt][e] = E::pack(ex[kb][8 * tt + 2 * e], ex[kb][8 * tt + 2 * e + 1]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Phase boundary: this wave's LDS reads are complete, then a workgroup barrier that the
@@ -511,9 +546,9 @@ void fa_fwd_kernel(const KernelArgs p) {
   }
 
   // ---- epilogue: O = O~ / l, LSE = ln(l) + m; both half-waves hold partial sums --------
-  if (wrow0 >= slen) return;
+  if (wrow0 >= slen || wrow0 + 32 <= 0) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < slen) {
+  if (qrow >= 0 && qrow < slen) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = p.o + bidx * p.o_sb + h * p.o_sh + int64_t(seq0 + qrow) * p.o_sn;
 #pragma unroll
@@ -575,7 +610,7 @@ fa_status launch_forward(const fa_fwd_params& p, void* stream, const char** hip_
   a.c = float(c);
   a.q_and = p.scale == 0.f ? 0u : 0xFFFFFFFFu;
   a.q_xor = p.scale < 0.f ? 0x80008000u : 0u;
-  a.xcd_group = varlen ? 0 : 1;
+  a.xcd_group = p.heads_kv % 8 == 0 ? 2 : (varlen ? 0 : 1);
   const int groups = varlen ? p.num_seqs : p.batch;
   const int grid = a.n_qblocks * p.heads_q * groups;
   hipStream_t s = static_cast<hipStream_t>(stream);

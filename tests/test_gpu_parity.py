@@ -66,6 +66,20 @@ def test_packed_variable_lengths(dtype, d, causal):
     assert_close(o, lse, o_ref, lse_ref, dtype, "varlen")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv,lens", [(8, 8, None), (16, 8, None), (8, 8, (0, 129, 300, 5, 520)),
+                                         (24, 8, (257, 1, 64))])
+def test_kv_heads_dealt_over_xcds(hq, hkv, lens, causal):
+    """heads_kv a multiple of 8 selects the head-strided workgroup order (every XCD takes every
+    eighth kv head with its query heads); the result must not depend on the order."""
+    n = 300 if lens is None else sum(lens)
+    inp = si.random_inputs(1 if lens else 2, hq, hkv, n, 64, si.F16, seed=hq + hkv + n,
+                           causal=causal, seq_lens=lens)
+    o, lse = run(inp)
+    o_ref, lse_ref = _oracle(inp)
+    assert_close(o, lse, o_ref, lse_ref, si.F16, f"heads {hq}/{hkv} lens={lens}")
+
+
 def test_packed_with_larger_max_seqlen_bound():
     """max_seqlen only sizes the grid: a loose upper bound gives the same result."""
     lens = (100, 260, 3)
