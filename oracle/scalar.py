@@ -39,12 +39,20 @@ def online_softmax_two_pass(chunks: Sequence[Sequence[float]]) -> Tuple[List[flo
 def attention_scalar(q: Sequence[Sequence[float]], k: Sequence[Sequence[float]],
                      v: Sequence[Sequence[float]], scale: float,
                      causal: bool = False) -> Tuple[List[List[float]], List[float]]:
-    """One head, lists of rows. Returns (O rows, lse per row)."""
+    """One head, lists of rows. Returns (O rows, lse per row).
+
+    The queries are the last len(q) positions of the len(k) keys, so with causal a query i sees
+    the keys j <= i + len(k) - len(q); a query that sees no key gets O = 0 and lse = -inf.
+    """
     n = len(q)
-    d = len(v[0])
+    d = len(v[0]) if len(v) else len(q[0])
     o_rows, lses = [], []
     for i in range(n):
-        keys = range(i + 1) if causal else range(len(k))
+        keys = range(max(0, min(len(k), i + len(k) - n + 1))) if causal else range(len(k))
+        if len(keys) == 0:
+            o_rows.append([0.0] * d)
+            lses.append(-math.inf)
+            continue
         s = [scale * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in keys]
         m = max(s)
         e = [math.exp(t - m) for t in s]

@@ -5,14 +5,16 @@ storage dtype (fp16 or bf16, round-to-nearest-even) and decodes stored bit patte
 float64. Both the HIP path and the fp64 oracle consume exactly the same bit patterns, so a
 parity tolerance measures the kernel's error and not the input quantisation.
 
-The five workloads mirror the problem statement of the forward pass (Q, K, V and O as
+The first five workloads mirror the problem statement of the forward pass (Q, K, V and O as
 batch x heads x N x d, a scale, a causal flag, a GQA head ratio, packed variable-length
 sequences). The shape of the second one is the SDPA usage example on the FromZero2AI page
 ("FlashAttention: GPU Memory-Bound Speedups for Long-Context LLMs", section "Code Verification").
+The sixth is a query chunk against a longer key/value context (chunked prefill with a KV
+cache, xspy page "FlashAttention and chunked prefill mechanics", section 1).
 
 Draw order per workload: (varlen only) the sequence lengths, then Q, then K, then V, each as
-float32 standard normals in C order of shape [B, H, N, d]; the optional multiplier is applied
-before rounding.
+float32 standard normals in C order of shape [B, H, N, d] (K and V with the key length); the
+optional multiplier is applied before rounding.
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ class Workload:
     seed: int
     qk_multiplier: float = 1.0
     seq_lens: Optional[Tuple[int, ...]] = None  # varlen only (batch == 1)
+    seqlen_k: Optional[int] = None  # keys per batch entry when it differs from seqlen
 
     @property
     def scale(self) -> float:
@@ -58,11 +61,20 @@ class Workload:
     def max_seqlen(self) -> int:
         return max(self.seq_lens) if self.seq_lens is not None else self.seqlen
 
+    @property
+    def keys(self) -> int:
+        return self.seqlen if self.seqlen_k is None else self.seqlen_k
+
     def flops(self) -> float:
         """FLOPs by the metric convention: 4*N^2*d per (batch, head), halved when causal.
 
-        For packed sequences the count is summed per sequence.
+        For packed sequences the count is summed per sequence. With Nq queries against Nk keys
+        it is 4*Nq*Nk*d, less 2*Nq^2*d when causal (the same convention at Nq == Nk).
         """
+        if self.seqlen_k is not None:
+            nq, nk = self.seqlen, self.seqlen_k
+            per = 4.0 * self.head_dim * (nq * nk - (nq * nq / 2.0 if self.causal else 0.0))
+            return per * self.heads_q * self.batch
         lens = self.seq_lens if self.seq_lens is not None else (self.seqlen,) * self.batch
         per = sum(4.0 * n * n * self.head_dim for n in lens) * self.heads_q
         return per / 2.0 if self.causal else per
@@ -88,6 +100,8 @@ WORKLOADS: Dict[str, Workload] = {
                  qk_multiplier=1.5),
         Workload("gqa_b1_hq32_hkv8_n32768_d128_causal_bf16", 1, 32, 8, 32768, 128, BF16, True, 4),
         _c5(),
+        Workload("chunk_b1_hq32_hkv8_q2048_k16384_d128_causal_bf16", 1, 32, 8, 2048, 128, BF16,
+                 True, 6, seqlen_k=16384),
     ]
 }
 WORKLOAD_ORDER: List[str] = list(WORKLOADS)
@@ -147,6 +161,7 @@ class Inputs:
     scale: float
     causal: bool
     cu_seqlens: Optional[np.ndarray] = None
+    cu_seqlens_k: Optional[np.ndarray] = None  # packed keys, when packed unlike the queries
 
     @property
     def shape(self) -> Tuple[int, int, int, int, int]:
@@ -161,15 +176,25 @@ class Inputs:
 def random_inputs(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int,
                   dtype: str, seed: int, *, causal: bool = False, scale: Optional[float] = None,
                   qk_multiplier: float = 1.0, seq_lens: Optional[Tuple[int, ...]] = None,
-                  std: float = 1.0) -> Inputs:
-    """Q, K, V ~ N(0, std^2) (Q and K times qk_multiplier) rounded to dtype, from one seed."""
+                  std: float = 1.0, seqlen_k: Optional[int] = None,
+                  seq_lens_k: Optional[Tuple[int, ...]] = None) -> Inputs:
+    """Q, K, V ~ N(0, std^2) (Q and K times qk_multiplier) rounded to dtype, from one seed.
+
+    K and V have seqlen_k tokens (default seqlen); packed keys follow seq_lens_k (default
+    seq_lens)."""
     rng = np.random.default_rng(seed)
     if seq_lens is not None:
         if batch != 1 or sum(seq_lens) != seqlen:
             raise ValueError("packed sequences need batch == 1 and seqlen == sum(seq_lens)")
+    nk = seqlen if seqlen_k is None else seqlen_k
+    if seq_lens_k is not None:
+        if seq_lens is None or len(seq_lens_k) != len(seq_lens) or sum(seq_lens_k) != nk:
+            raise ValueError("seq_lens_k needs seq_lens of the same count and sums to seqlen_k")
+    elif seq_lens is not None and nk != seqlen:
+        raise ValueError("packed keys of another length need seq_lens_k")
     q = rng.standard_normal((batch, heads_q, seqlen, head_dim), dtype=np.float32)
-    k = rng.standard_normal((batch, heads_kv, seqlen, head_dim), dtype=np.float32)
-    v = rng.standard_normal((batch, heads_kv, seqlen, head_dim), dtype=np.float32)
+    k = rng.standard_normal((batch, heads_kv, nk, head_dim), dtype=np.float32)
+    v = rng.standard_normal((batch, heads_kv, nk, head_dim), dtype=np.float32)
     if std != 1.0:
         q *= np.float32(std)
         k *= np.float32(std)
@@ -177,18 +202,20 @@ def random_inputs(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim
     if qk_multiplier != 1.0:
         q *= np.float32(qk_multiplier)
         k *= np.float32(qk_multiplier)
-    cu = None
+    cu = cu_k = None
     if seq_lens is not None:
         cu = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int32)
+    if seq_lens_k is not None:
+        cu_k = np.concatenate([[0], np.cumsum(seq_lens_k)]).astype(np.int32)
     return Inputs(round_to_bits(q, dtype), round_to_bits(k, dtype), round_to_bits(v, dtype),
-                  dtype, 1.0 / math.sqrt(head_dim) if scale is None else scale, causal, cu)
+                  dtype, 1.0 / math.sqrt(head_dim) if scale is None else scale, causal, cu, cu_k)
 
 
 def workload_inputs(w: Workload) -> Inputs:
     """The seeded inputs of a named workload (the varlen lengths are part of the workload)."""
     return random_inputs(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, w.dtype, w.seed,
                          causal=w.causal, scale=w.scale, qk_multiplier=w.qk_multiplier,
-                         seq_lens=w.seq_lens)
+                         seq_lens=w.seq_lens, seqlen_k=w.seqlen_k)
 
 
 # ----------------------------------------------------------------------------------------

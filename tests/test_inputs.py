@@ -46,7 +46,7 @@ def test_same_seed_same_bits():
 
 def test_named_workloads():
     w = si.WORKLOADS
-    assert list(w) == si.WORKLOAD_ORDER and len(w) == 5
+    assert list(w) == si.WORKLOAD_ORDER and len(w) == 6
     c5 = w["varlen16_h16_d128_causal_bf16"]
     assert c5.seq_lens == (5664, 6695, 685, 6717, 4113, 4470, 5352, 2707, 8035, 926, 2646,
                            3456, 4899, 3649, 1518, 859)
@@ -56,6 +56,21 @@ def test_named_workloads():
     assert math.isclose(c3.flops(), 32 * 4 * 16384 ** 2 * 128 / 2)
     assert math.isclose(c3.scale, 0.08838834764831843)
     assert w["gqa_b1_hq32_hkv8_n32768_d128_causal_bf16"].heads_kv == 8
+    ch = w["chunk_b1_hq32_hkv8_q2048_k16384_d128_causal_bf16"]
+    assert (ch.seqlen, ch.keys) == (2048, 16384)
+    # causal chunk: query i of 2048 sees 16384 - 2048 + i + 1 keys; 4*d per key, 32 heads
+    exact = 4 * 128 * 32 * sum(16384 - 2048 + i + 1 for i in range(2048))
+    assert abs(ch.flops() - exact) / exact < 1e-3
+
+
+def test_key_length_inputs():
+    a = si.random_inputs(1, 4, 2, 10, 64, si.F16, 3, seqlen_k=25)
+    assert a.q.shape == (1, 4, 10, 64) and a.k.shape == (1, 2, 25, 64) == a.v.shape
+    b = si.random_inputs(1, 2, 2, 6, 64, si.F16, 3, seq_lens=(2, 4), seqlen_k=13,
+                         seq_lens_k=(9, 4))
+    assert list(b.cu_seqlens) == [0, 2, 6] and list(b.cu_seqlens_k) == [0, 9, 13]
+    with pytest.raises(ValueError):
+        si.random_inputs(1, 2, 2, 6, 64, si.F16, 3, seq_lens=(2, 4), seqlen_k=13)
 
 
 def test_row_sample_has_edges_and_stays_in_range():

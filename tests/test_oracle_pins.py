@@ -335,6 +335,91 @@ def test_row_evaluation_matches_full_evaluation(causal):
 
 
 # ------------------------------------------------------------------------------------------
+# Queries and keys of different lengths (a query chunk against a key/value cache)
+# ------------------------------------------------------------------------------------------
+
+def test_chunked_prefill_rows_equal_full_causal_rows():
+    """Chunked prefill (xspy page, section 1; the notes' KV-cache composability) computes the
+    same rows as full causal attention: the last c queries against all N keys and values give
+    exactly the last c rows of causal self-attention over N tokens."""
+    q, k, v = _qkv(1, 2, 1, 37, 8, seed=40)
+    o, lse = attention(q, k, v, 0.45, True)
+    for c in (1, 5, 36, 37):
+        oc, lc = attention(q[:, :, -c:], k, v, 0.45, True)
+        np.testing.assert_allclose(oc, o[:, :, -c:], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lc, lse[:, :, -c:], rtol=1e-14, atol=0)
+
+
+def test_packed_chunks_equal_full_causal_rows():
+    """The same for packed sequences, each with its own chunk length and key length."""
+    full = [7, 12, 1, 9]
+    chunk = [3, 12, 1, 0]
+    q, k, v = _qkv(1, 2, 2, sum(full), 4, seed=41)
+    cu_full = np.concatenate([[0], np.cumsum(full)])
+    cu_chunk = np.concatenate([[0], np.cumsum(chunk)])
+    o, lse = attention(q, k, v, 0.7, True, cu_seqlens=cu_full)
+    take = np.concatenate([np.arange(e - c, e) for e, c in zip(cu_full[1:], chunk)]).astype(int)
+    oc, lc = attention(q[:, :, take], k, v, 0.7, True, cu_seqlens=cu_chunk, cu_seqlens_k=cu_full)
+    np.testing.assert_allclose(oc, o[:, :, take], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lc, lse[:, :, take], rtol=1e-14, atol=0)
+
+
+def test_chunk_longer_than_keys_has_empty_rows():
+    """With more queries than keys the first Nq - Nk causal rows see no key (reading: O = 0,
+    LSE = -inf); the others are causal self-attention over the Nk keys."""
+    q, k, v = _qkv(1, 1, 1, 9, 4, seed=42)
+    k, v = k[:, :, :4], v[:, :, :4]
+    o, lse = attention(q, k, v, 0.9, True)
+    assert np.all(o[0, 0, :5] == 0.0) and np.all(np.isneginf(lse[0, 0, :5]))
+    o2, l2 = attention(q[:, :, 5:], k, v, 0.9, True)
+    np.testing.assert_array_equal(o[:, :, 5:], o2)
+    np.testing.assert_array_equal(lse[:, :, 5:], l2)
+    o3, l3 = attention(q, k[:, :, :0], v[:, :, :0], 0.9, False)
+    assert np.all(o3 == 0.0) and np.all(np.isneginf(l3))
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1), (1, 6), (2, 5), (4, 4), (5, 2), (3, 0)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny_unequal_lengths(nq, nk, causal):
+    r = _rng(nq * 10 + nk)
+    q, k, v = r.standard_normal((1, 1, nq, 3)), r.standard_normal((1, 1, nk, 3)), \
+        r.standard_normal((1, 1, nk, 3))
+    o, lse = attention(q, k, v, 0.8, causal)
+    o_s, lse_s = scalar.attention_scalar(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(),
+                                         0.8, causal)
+    np.testing.assert_allclose(o[0, 0], np.array(o_s), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], np.array(lse_s), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("nq,nk", [(3, 17), (17, 3), (1, 40)])
+def test_unequal_lengths_match_torch_sdpa_float64(nq, nk):
+    """Non-causal attention with Nq != Nk against PyTorch SDPA in float64."""
+    r = _rng(nq + 100 * nk)
+    q = r.standard_normal((2, 4, nq, 8))
+    k, v = r.standard_normal((2, 2, nk, 8)), r.standard_normal((2, 2, nk, 8))
+    o, lse = attention(q, k, v, 0.3, False)
+    o_t, lse_t = _sdpa(q, k, v, 0.3, False)
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_t, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_evaluation_matches_full_evaluation_unequal_lengths(causal):
+    full = [9, 3, 20]
+    chunk = [4, 3, 0]
+    cu_k = np.concatenate([[0], np.cumsum(full)])
+    cu_q = np.concatenate([[0], np.cumsum(chunk)])
+    r = _rng(43)
+    q = r.standard_normal((1, 4, sum(chunk), 8))
+    k, v = r.standard_normal((1, 2, sum(full), 8)), r.standard_normal((1, 2, sum(full), 8))
+    o, lse = attention(q, k, v, 0.5, causal, cu_seqlens=cu_q, cu_seqlens_k=cu_k)
+    rows = [(0, h, i) for h in range(4) for i in range(sum(chunk))]
+    o_r, lse_r = attention_rows(q, k, v, 0.5, causal, rows, cu_seqlens=cu_q, cu_seqlens_k=cu_k)
+    np.testing.assert_allclose(o_r, o.reshape(-1, 8), atol=1e-14)
+    np.testing.assert_allclose(lse_r, lse.reshape(-1), rtol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
 # Planted mistakes: each must be caught by at least one of the pins above
 # ------------------------------------------------------------------------------------------
 
@@ -347,6 +432,7 @@ def _pin_failures():
         lambda: test_causal_first_row_sees_only_itself(),
         lambda: test_uniform_when_scores_vanish(True),
         lambda: test_p1_example2_embedded_in_attention(),
+        lambda: test_chunked_prefill_rows_equal_full_causal_rows(),
     ]
     for i, chk in enumerate(checks):
         try:
@@ -362,10 +448,15 @@ def test_pins_pass_on_the_oracle():
 
 
 MUTANTS = {
-    "causal_excludes_diagonal": ("_allowed", lambda n, causal: (
-        np.arange(n)[None, :] < np.arange(n)[:, None]) if causal else np.ones((n, n), bool)),
-    "causal_off_by_one_late": ("_allowed", lambda n, causal: (
-        np.arange(n)[None, :] <= np.arange(n)[:, None] + 1) if causal else np.ones((n, n), bool)),
+    "causal_excludes_diagonal": ("_allowed", lambda nq, nk, causal: (
+        np.arange(nk)[None, :] < np.arange(nq)[:, None] + (nk - nq)) if causal
+        else np.ones((nq, nk), bool)),
+    "causal_off_by_one_late": ("_allowed", lambda nq, nk, causal: (
+        np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq) + 1) if causal
+        else np.ones((nq, nk), bool)),
+    "chunk_aligned_to_key_start": ("_allowed", lambda nq, nk, causal: (
+        np.arange(nk)[None, :] <= np.arange(nq)[:, None]) if causal
+        else np.ones((nq, nk), bool)),
     "scale_dropped": ("_head_scores", lambda qh, kh, scale: qh @ kh.T),
     "scores_transposed": ("_head_scores", lambda qh, kh, scale: scale * (kh @ qh.T)),
     "gqa_heads_interleaved": ("kv_head", lambda h, hq, hkv: h % hkv),
