@@ -78,8 +78,10 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
                 s0, s1 = int(cu[s]), int(cu[s + 1])
             else:
                 s0, s1 = 0, w.seqlen
-            keys = (i - s0 + 1) if w.causal else (s1 - s0)
-            flops += 4.0 * keys * w.head_dim
+            nk = w.keys if cu is None else s1 - s0  # keys of the row's sequence
+            shift = nk - (s1 - s0)  # the queries are the last positions of the keys
+            keys = min(nk, i - s0 + shift + 1) if w.causal else nk
+            flops += 4.0 * max(keys, 0) * w.head_dim
         done += len(chunk)
     elapsed = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()
@@ -215,10 +217,13 @@ def main() -> int:
             "heads_q": w.heads_q,
             "heads_kv": w.heads_kv,
             "seqlen": w.seqlen,
+            "seqlen_k": w.keys,
             "head_dim": w.head_dim,
             "causal": w.causal,
             "flop_count": flops,
-            "flop_convention": "4*N^2*d per (batch, head), halved for causal",
+            "flop_convention": ("4*N^2*d per (batch, head), halved for causal"
+                                if w.seqlen_k is None else
+                                "4*Nq*Nk*d per (batch, head), less 2*Nq^2*d for causal"),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {

@@ -23,7 +23,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 FA_F16, FA_BF16 = 0, 1
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 1
+FA_ABI_VERSION = 2
 
 _I64x3 = ctypes.c_int64 * 3
 
@@ -53,6 +53,9 @@ class FaFwdParams(ctypes.Structure):
         ("k_stride", _I64x3),
         ("v_stride", _I64x3),
         ("o_stride", _I64x3),
+        ("seqlen_k", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("cu_seqlens_k", ctypes.c_void_p),
     ]
 
     def __init__(self, **kw):
@@ -118,14 +121,18 @@ _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
 
 def _strides(t: torch.Tensor):
+    if t.numel() == 0:  # no element is addressed: report the contiguous layout
+        return _I64x3(t.shape[1] * t.shape[2] * t.shape[3], t.shape[2] * t.shape[3], t.shape[3])
     s = t.stride()
     return _I64x3(s[0], s[1], s[2])
 
 
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                 lse: torch.Tensor, scale: float, causal: bool,
-                cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int]) -> FaFwdParams:
-    """Fills FaFwdParams from [B, H, N, d] tensors (strides in elements)."""
+                cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int],
+                cu_seqlens_k: Optional[torch.Tensor] = None) -> FaFwdParams:
+    """Fills FaFwdParams from [B, H, N, d] tensors (strides in elements); K and V may have
+    their own token count."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v and o must be 4-D [batch, heads, tokens, head_dim]")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
@@ -133,18 +140,18 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [batch, heads_q, tokens]")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if t.stride(3) != 1 and t.shape[3] > 1:
+        if t.stride(3) != 1 and t.shape[3] > 1 and t.numel() > 0:
             raise ValueError(f"{name}: the head_dim dimension must be contiguous")
     b, hq, n, d = q.shape
-    hkv = k.shape[1]
-    if tuple(k.shape) != (b, hkv, n, d) or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("k and v must be [batch, heads_kv, tokens, head_dim] matching q")
+    hkv, nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (b, hkv, nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [batch, heads_kv, key tokens, head_dim] matching q")
     if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (b, hq, n):
         raise ValueError("o must match q and lse must be [batch, heads_q, tokens]")
     p = FaFwdParams(
         dtype=_DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
         o=o.data_ptr(), lse=lse.data_ptr(), batch=b, heads_q=hq, heads_kv=hkv, seqlen=n,
-        head_dim=d, causal=int(bool(causal)), scale=float(scale),
+        seqlen_k=nk, head_dim=d, causal=int(bool(causal)), scale=float(scale),
         q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o))
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
@@ -156,19 +163,29 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
         p.cu_seqlens = cu_seqlens.data_ptr()
         p.num_seqs = cu_seqlens.numel() - 1
         p.max_seqlen = int(max_seqlen)
+    if cu_seqlens_k is not None:
+        if cu_seqlens is None:
+            raise ValueError("cu_seqlens_k needs cu_seqlens")
+        if (cu_seqlens_k.dtype != torch.int32 or cu_seqlens_k.dim() != 1
+                or cu_seqlens_k.numel() != cu_seqlens.numel()):
+            raise ValueError("cu_seqlens_k must be a 1-D int32 tensor shaped like cu_seqlens")
+        if cu_seqlens_k.device != q.device:
+            raise ValueError("cu_seqlens_k must live on the same device as q")
+        p.cu_seqlens_k = cu_seqlens_k.data_ptr()
     return p
 
 
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
            lse: torch.Tensor, *, scale: float, causal: bool = False,
            cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
-           stream: Optional[torch.cuda.Stream] = None) -> None:
+           stream: Optional[torch.cuda.Stream] = None,
+           cu_seqlens_k: Optional[torch.Tensor] = None) -> None:
     """Enqueues the forward pass writing o and lse, on `stream` (default: torch's current)."""
     lib = load_library()
     for t in (q, k, v, o, lse):
         if not t.is_cuda:
             raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
-    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen)
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         st = int(lib.fa_fwd(ctypes.byref(p), ctypes.c_void_p(s.cuda_stream)))
@@ -178,13 +195,16 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
               scale: Optional[float] = None, causal: bool = False,
-              cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None
+              cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+              cu_seqlens_k: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, torch.Tensor]:
     """softmax(scale * Q K^T) V and its per-row log-sum-exp, for [B, H, N, d] tensors.
 
-    scale defaults to 1/sqrt(d). With cu_seqlens (int32 prefix sums, batch 1) sequences are
-    packed along the token axis and attend only within themselves; max_seqlen, if omitted,
-    is read from cu_seqlens with a device-to-host copy.
+    scale defaults to 1/sqrt(d). K and V may hold more (or fewer) tokens than Q: the queries
+    are then the last positions of the keys, which is what causal masking measures from. With
+    cu_seqlens (int32 prefix sums, batch 1) sequences are packed along the token axis and
+    attend only within themselves (keys per cu_seqlens_k when packed differently); max_seqlen,
+    if omitted, is read from cu_seqlens with a device-to-host copy.
     """
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
@@ -194,7 +214,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
-           max_seqlen=max_seqlen)
+           max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k)
     return o, lse
 
 

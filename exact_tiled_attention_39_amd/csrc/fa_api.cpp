@@ -16,6 +16,13 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // Strides are element counts for (batch, head, token). All must be non-negative multiples of
 // 8 (16-byte rows); token rows may not overlap, and a token stride is at most 2^23 elements so
 // that the byte extent of one 64-row K/V tile fits a 32-bit buffer range.
+// a * b * c > limit, for non-negative factors, without overflowing int64.
+bool product_exceeds(int64_t a, int64_t b, int64_t c, int64_t limit) {
+  if (a == 0 || b == 0 || c == 0) return false;
+  if (a > limit / b) return true;
+  return a * b > limit / c;
+}
+
 bool stride_ok(const int64_t s[3], int32_t head_dim, int32_t seqlen) {
   for (int i = 0; i < 3; ++i)
     if (s[i] < 0 || (s[i] & 7) != 0) return false;
@@ -37,29 +44,37 @@ fa_status fa_check_args(const fa_fwd_params* p) {
   if (p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(p->scale)) return FA_ERR_UNSUPPORTED;
-  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seqlen < 0) return FA_ERR_SHAPE;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seqlen < 0 || p->seqlen_k < 0 ||
+      p->reserved0 != 0)
+    return FA_ERR_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return FA_ERR_GQA;
   if (p->cu_seqlens != nullptr) {
     if (p->batch != 1 || p->num_seqs < 1) return FA_ERR_VARLEN;
     if (p->max_seqlen < 0 || p->max_seqlen > p->seqlen) return FA_ERR_VARLEN;
     if (p->seqlen > 0 && p->max_seqlen < 1) return FA_ERR_VARLEN;
+    if (p->cu_seqlens_k == nullptr && p->seqlen_k != p->seqlen) return FA_ERR_VARLEN;
+  } else if (p->cu_seqlens_k != nullptr) {
+    return FA_ERR_VARLEN;
   }
   if (p->seqlen == 0) return FA_OK;
-  if (!p->q || !p->k || !p->v || !p->o || !p->lse) return FA_ERR_NULL;
+  // k and v may be NULL only when there are no keys at all
+  if (!p->q || !p->o || !p->lse || (p->seqlen_k > 0 && (!p->k || !p->v))) return FA_ERR_NULL;
   if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
     return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0) return FA_ERR_ALIGN;
   if (!stride_ok(p->q_stride, p->head_dim, p->seqlen) ||
-      !stride_ok(p->k_stride, p->head_dim, p->seqlen) ||
-      !stride_ok(p->v_stride, p->head_dim, p->seqlen) ||
+      !stride_ok(p->k_stride, p->head_dim, p->seqlen_k) ||
+      !stride_ok(p->v_stride, p->head_dim, p->seqlen_k) ||
       !stride_ok(p->o_stride, p->head_dim, p->seqlen))
     return FA_ERR_ALIGN;
-  // At most one workgroup per (128 query rows, query head, batch entry or sequence).
+  // The kernel runs one workgroup per (256 query rows, query head, batch entry or sequence);
+  // the bound below counts 128-row blocks, so it is conservative.
   const int64_t rows = p->cu_seqlens ? p->max_seqlen : p->seqlen;
   const int64_t groups = p->cu_seqlens ? p->num_seqs : p->batch;
-  const int64_t grid = ((rows + 127) / 128) * int64_t(p->heads_q) * groups;
-  if (grid > INT32_MAX) return FA_ERR_SHAPE;
-  if (int64_t(p->batch) * p->heads_q * int64_t(p->seqlen) > INT64_MAX / 4) return FA_ERR_SHAPE;
+  if (product_exceeds((rows + 127) / 128, p->heads_q, groups, INT32_MAX)) return FA_ERR_SHAPE;
+  // element counts of Q/O/LSE and of K/V stay far inside int64
+  if (product_exceeds(p->batch, p->heads_q, p->seqlen, INT64_MAX / 4)) return FA_ERR_SHAPE;
+  if (product_exceeds(p->batch, p->heads_kv, p->seqlen_k, INT64_MAX / 4)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -87,7 +102,8 @@ const char* fa_status_string(int32_t status) {
     case FA_ERR_GQA: return "FA_ERR_GQA: heads_q must be a multiple of heads_kv";
     case FA_ERR_VARLEN:
       return "FA_ERR_VARLEN: cu_seqlens needs batch == 1, num_seqs >= 1 and "
-             "1 <= max_seqlen <= seqlen";
+             "1 <= max_seqlen <= seqlen; cu_seqlens_k needs cu_seqlens, and packed keys of "
+             "another total length need cu_seqlens_k";
     case FA_ERR_ABI: return "FA_ERR_ABI: struct_size does not match sizeof(fa_fwd_params)";
     case FA_ERR_LAUNCH: return g_last_hip_error;
     default: return "unknown fa_status";

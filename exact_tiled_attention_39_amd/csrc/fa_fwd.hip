@@ -75,11 +75,13 @@ struct KernelArgs {
   uint16_t* o;
   float* lse;
   const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens_k;  // key ranges of the packed sequences (== cu_seqlens by default)
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
   int64_t v_sb, v_sh, v_sn;
   int64_t o_sb, o_sh, o_sn;
-  int32_t seqlen;     // tokens per batch entry (packed total for varlen)
+  int32_t seqlen;     // query tokens per batch entry (packed total for varlen)
+  int32_t seqlen_k;   // key tokens per batch entry (unused for varlen)
   int32_t heads_q;
   int32_t group;      // heads_q / heads_kv
   int32_t n_qblocks;  // query blocks per (batch entry or sequence, head)
@@ -239,12 +241,17 @@ void fa_fwd_kernel(const KernelArgs p) {
     b = bh / p.heads_q;
     h = bh - b * p.heads_q;
   }
-  int seq0 = 0, slen = p.seqlen, bidx = b;
+  int seq0 = 0, slen = p.seqlen, kseq0 = 0, klen = p.seqlen_k, bidx = b;
   if (VARLEN) {
     seq0 = p.cu_seqlens[b];
     slen = p.cu_seqlens[b + 1] - seq0;
+    kseq0 = p.cu_seqlens_k[b];
+    klen = p.cu_seqlens_k[b + 1] - kseq0;
     bidx = 0;
   }
+  // The queries are the last slen of the klen key positions: causal query i sees keys
+  // j <= i + shift (shift = 0 for self-attention).
+  const int shift = klen - slen;
   // Causal blocks are aligned to the sequence end (shifted down by pad rows), so a partial
   // block is block 0, which sees the fewest keys (its rows below 0 are idle); block u then
   // sees 4 u + ceil((256 - pad) / 64) key tiles, and the order stays heaviest first.
@@ -255,11 +262,12 @@ void fa_fwd_kernel(const KernelArgs p) {
   const int hk = h / p.group;
 
   const uint16_t* qb = p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0) * p.q_sn;
-  const uint16_t* kbase = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
-  const uint16_t* vbase = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
+  const uint16_t* kbase = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(kseq0) * p.k_sn;
+  const uint16_t* vbase = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(kseq0) * p.v_sn;
 
-  const int kv_end = CAUSAL ? q0 + kBlockM : slen;
-  const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+  // keys [0, kv_end) are visible to some row of the block (none when kv_end <= 0)
+  const int kv_end = CAUSAL ? min(klen, q0 + kBlockM + shift) : klen;
+  const int n_tiles = kv_end > 0 ? (kv_end + kBlockN - 1) / kBlockN : 0;
 
   // ---- Q^T fragments (B operand), resident for the whole kernel -----------------------
   // The two waves sharing a SIMD (w and w + 4) take neighbouring 32-row slices, so both
@@ -314,7 +322,7 @@ void fa_fwd_kernel(const KernelArgs p) {
   auto dma = [&](auto st, int tile) __attribute__((always_inline)) {
     constexpr int ST = decltype(st)::value;
     const int key0 = tile * kBlockN;
-    const int rows = min(slen - key0, kBlockN);  // rows of this tile inside the sequence
+    const int rows = min(klen - key0, kBlockN);  // rows of this tile inside the sequence
     const int bytes = int((rows - 1) * ld_sn * 2) + D * 2;
     const u32x4 rsrc = make_rsrc(ld_base + int64_t(key0) * ld_sn, bytes);
     const uint32_t dst = lds_ring + (grp ? kStages * G::kKBytes + ST * G::kVBytes
@@ -416,10 +424,10 @@ void fa_fwd_kernel(const KernelArgs p) {
   auto softmax = [&](int tile) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     const int key0 = tile * kBlockN;
-    const bool edge = (key0 + kBlockN > slen) || (CAUSAL && key0 + kBlockN - 1 > wrow0);
+    const bool edge = (key0 + kBlockN > klen) || (CAUSAL && key0 + kBlockN - 1 > wrow0 + shift);
     if (edge) {
       // entry i of key half kb is key key0 + off + 4 half; it is visible while off <= lim
-      const int lim = (CAUSAL ? min(slen - 1, qrow) : slen - 1) - key0 - 4 * half;
+      const int lim = (CAUSAL ? min(klen - 1, qrow + shift) : klen - 1) - key0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -492,56 +500,60 @@ void fa_fwd_kernel(const KernelArgs p) {
   // for K_{p+1} before that slot's closing barrier.
   // V_p is read in slots 2p + 2, 2p + 3; group 1 issues V_{p+2} in slot 2p and has waited
   // for V_p before the closing barrier of slot 2p + 1.
-  // Both groups execute 2 (n_tiles + 1) barriers after the prologue's one.
-  {
-    // V stage 3 is read (with P = 0) before any tile lands there: it must hold finite data.
-    const u32x4 zero = u32x4{0, 0, 0, 0};
-    for (int off = tid * 16; off < G::kVBytes; off += kThreads * 16)
-      *reinterpret_cast<u32x4*>(lds_v + 3 * G::kVBytes + off) = zero;
-  }
-  if (grp == 0) {
-    dma(Int<0>{}, 0);
-    if (n_tiles > 1) dma(Int<1>{}, 1);
-    if (n_tiles > 2) dma(Int<2>{}, 2);
-    dma_wait(min(n_tiles - 1, 2));  // K_0 in LDS
-  } else {
-    dma(Int<0>{}, 0);
-    if (n_tiles > 1) dma(Int<1>{}, 1);
-  }
-  __syncthreads();
-
-  // one ring step of each group; ST = p % 4
-  auto step_g0 = [&](auto st, int tile) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
-    phase_sync();
-    if (tile < n_tiles) softmax(tile);
-    if (tile + 3 < n_tiles) dma(Int<(ST + 3) & 3>{}, tile + 3);
-    if (tile + 1 < n_tiles) dma_wait(min(n_tiles - 2 - tile, 2));  // K_{tile+1} in LDS
-    phase_sync();
-  };
-  auto step_g1 = [&](auto st, int tile) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st)::value;
-    if (tile >= 1) softmax(tile - 1);
-    if (tile + 2 < n_tiles) dma(Int<(ST + 2) & 3>{}, tile + 2);
-    phase_sync();
-    phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
-    if (tile < n_tiles) dma_wait(min(n_tiles - 1 - tile, 2));  // V_tile in LDS
-    phase_sync();
-  };
-  if (grp == 0) {
-    for (int tile = 0; tile <= n_tiles; tile += 4) {
-      step_g0(Int<0>{}, tile);
-      if (tile + 1 <= n_tiles) step_g0(Int<1>{}, tile + 1);
-      if (tile + 2 <= n_tiles) step_g0(Int<2>{}, tile + 2);
-      if (tile + 3 <= n_tiles) step_g0(Int<3>{}, tile + 3);
+  // Both groups execute 2 (n_tiles + 1) barriers after the prologue's one. A block whose
+  // rows see no key at all (n_tiles == 0, only possible when keys are fewer than queries)
+  // skips the loop as a whole workgroup.
+  if (n_tiles > 0) {
+    {
+      // V stage 3 is read (with P = 0) before any tile lands there: it must hold finite data.
+      const u32x4 zero = u32x4{0, 0, 0, 0};
+      for (int off = tid * 16; off < G::kVBytes; off += kThreads * 16)
+        *reinterpret_cast<u32x4*>(lds_v + 3 * G::kVBytes + off) = zero;
     }
-  } else {
-    for (int tile = 0; tile <= n_tiles; tile += 4) {
-      step_g1(Int<0>{}, tile);
-      if (tile + 1 <= n_tiles) step_g1(Int<1>{}, tile + 1);
-      if (tile + 2 <= n_tiles) step_g1(Int<2>{}, tile + 2);
-      if (tile + 3 <= n_tiles) step_g1(Int<3>{}, tile + 3);
+    if (grp == 0) {
+      dma(Int<0>{}, 0);
+      if (n_tiles > 1) dma(Int<1>{}, 1);
+      if (n_tiles > 2) dma(Int<2>{}, 2);
+      dma_wait(min(n_tiles - 1, 2));  // K_0 in LDS
+    } else {
+      dma(Int<0>{}, 0);
+      if (n_tiles > 1) dma(Int<1>{}, 1);
+    }
+    __syncthreads();
+
+    // one ring step of each group; ST = p % 4
+    auto step_g0 = [&](auto st, int tile) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
+      phase_sync();
+      if (tile < n_tiles) softmax(tile);
+      if (tile + 3 < n_tiles) dma(Int<(ST + 3) & 3>{}, tile + 3);
+      if (tile + 1 < n_tiles) dma_wait(min(n_tiles - 2 - tile, 2));  // K_{tile+1} in LDS
+      phase_sync();
+    };
+    auto step_g1 = [&](auto st, int tile) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st)::value;
+      if (tile >= 1) softmax(tile - 1);
+      if (tile + 2 < n_tiles) dma(Int<(ST + 2) & 3>{}, tile + 2);
+      phase_sync();
+      phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
+      if (tile < n_tiles) dma_wait(min(n_tiles - 1 - tile, 2));  // V_tile in LDS
+      phase_sync();
+    };
+    if (grp == 0) {
+      for (int tile = 0; tile <= n_tiles; tile += 4) {
+        step_g0(Int<0>{}, tile);
+        if (tile + 1 <= n_tiles) step_g0(Int<1>{}, tile + 1);
+        if (tile + 2 <= n_tiles) step_g0(Int<2>{}, tile + 2);
+        if (tile + 3 <= n_tiles) step_g0(Int<3>{}, tile + 3);
+      }
+    } else {
+      for (int tile = 0; tile <= n_tiles; tile += 4) {
+        step_g1(Int<0>{}, tile);
+        if (tile + 1 <= n_tiles) step_g1(Int<1>{}, tile + 1);
+        if (tile + 2 <= n_tiles) step_g1(Int<2>{}, tile + 2);
+        if (tile + 3 <= n_tiles) step_g1(Int<3>{}, tile + 3);
+      }
     }
   }
 
@@ -549,7 +561,9 @@ void fa_fwd_kernel(const KernelArgs p) {
   if (wrow0 >= slen || wrow0 + 32 <= 0) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow >= 0 && qrow < slen) {
-    const float inv = 1.f / l_tot;
+    // a row that sees no key: O = 0, LSE = -inf (its sums are 0 or NaN and are not used)
+    const bool empty = (CAUSAL ? min(klen, qrow + shift + 1) : klen) <= 0;
+    const float inv = empty ? 0.f : 1.f / l_tot;
     uint16_t* orow = p.o + bidx * p.o_sb + h * p.o_sh + int64_t(seq0 + qrow) * p.o_sn;
 #pragma unroll
     for (int j = 0; j < kOBlocks; ++j) {
@@ -557,14 +571,15 @@ void fa_fwd_kernel(const KernelArgs p) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = j * 32 + 8 * g + 4 * half;
         u32x2 w;
-        w[0] = E::pack(oacc[j][4 * g + 0] * inv, oacc[j][4 * g + 1] * inv);
-        w[1] = E::pack(oacc[j][4 * g + 2] * inv, oacc[j][4 * g + 3] * inv);
+        w[0] = empty ? 0u : E::pack(oacc[j][4 * g + 0] * inv, oacc[j][4 * g + 1] * inv);
+        w[1] = empty ? 0u : E::pack(oacc[j][4 * g + 2] * inv, oacc[j][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
     }
     if (half == 0) {
       const float lse2 = m_run + __builtin_amdgcn_logf(l_tot);  // log2 units
-      p.lse[(int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + qrow] = lse2 * 0.69314718055994531f;
+      p.lse[(int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + qrow] =
+          empty ? -INFINITY : lse2 * 0.69314718055994531f;
     }
   }
 }
@@ -596,11 +611,13 @@ fa_status launch_forward(const fa_fwd_params& p, void* stream, const char** hip_
   a.o = static_cast<uint16_t*>(p.o);
   a.lse = p.lse;
   a.cu_seqlens = p.cu_seqlens;
+  a.cu_seqlens_k = p.cu_seqlens_k != nullptr ? p.cu_seqlens_k : p.cu_seqlens;
   a.q_sb = p.q_stride[0]; a.q_sh = p.q_stride[1]; a.q_sn = p.q_stride[2];
   a.k_sb = p.k_stride[0]; a.k_sh = p.k_stride[1]; a.k_sn = p.k_stride[2];
   a.v_sb = p.v_stride[0]; a.v_sh = p.v_stride[1]; a.v_sn = p.v_stride[2];
   a.o_sb = p.o_stride[0]; a.o_sh = p.o_stride[1]; a.o_sn = p.o_stride[2];
   a.seqlen = p.seqlen;
+  a.seqlen_k = p.seqlen_k;
   a.heads_q = p.heads_q;
   a.group = p.heads_q / p.heads_kv;
   const bool varlen = p.cu_seqlens != nullptr;

@@ -7,7 +7,8 @@
  *     O[b, h, i, :] = sum_j exp(s_ij - m_i) V[b, hk, j, :] / sum_j exp(s_ij - m_i)
  *     LSE[b, h, i]  = m_i + ln(sum_j exp(s_ij - m_i)),           m_i = max_j s_ij
  *
- * with hk = h / (heads_q / heads_kv). That is softmax(scale * Q K^T) V, the self-attention of the
+ * with hk = h / (heads_q / heads_kv); a query that sees no key at all gets O = 0 and
+ * LSE = -inf. That is softmax(scale * Q K^T) V, the self-attention of the
  * "Flash Attention" notes (14cs17, sections "Prerequisites" and "Standard Attention Memory
  * Analysis"), computed tile by tile with the online softmax of that page's Theorem 2 and the
  * algorithm of its section "Flash Attention Algorithm": blocks of queries stay on chip while
@@ -17,6 +18,11 @@
  * section "Flash Attention 2 Improvements". The log-sum-exp output, the causal mask, the head
  * grouping and the packed-sequence layout are not spelled out on the pages; the readings are:
  *   - causal: key j is visible to query i iff j <= i (positions inside the sequence);
+ *   - queries and keys of different lengths (a query chunk against a key/value cache: the notes
+ *     list the KV cache as composable with the method, section "Connection to the Broader
+ *     Curriculum"; the xspy page "FlashAttention and chunked prefill mechanics", section 1,
+ *     pairs it with chunked prefill): the Nq queries are the last Nq of the Nk key positions,
+ *     so causal visibility is j <= i + (Nk - Nq). With Nq == Nk this is the rule above;
  *   - grouped heads: query heads [g*r, (g+1)*r) share key/value head g, r = heads_q / heads_kv;
  *   - packed sequences: tokens of sequence s occupy [cu_seqlens[s], cu_seqlens[s+1]) and attend
  *     only inside that range;
@@ -38,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -55,7 +61,9 @@ typedef enum fa_status {
                              non-negative multiple of 8 elements, or a token stride is below
                              head_dim (overlapping rows) or above 2^23 elements */
   FA_ERR_GQA = 5,         /* heads_q is not a multiple of heads_kv */
-  FA_ERR_VARLEN = 6,      /* cu_seqlens given with batch != 1, num_seqs < 1 or a bad max_seqlen */
+  FA_ERR_VARLEN = 6,      /* cu_seqlens given with batch != 1, num_seqs < 1 or a bad max_seqlen;
+                             cu_seqlens_k without cu_seqlens; or packed queries whose keys
+                             differ in length without cu_seqlens_k */
   FA_ERR_ABI = 7,         /* struct_size does not match this library's fa_fwd_params */
   FA_ERR_LAUNCH = 8       /* the HIP launch failed (the HIP error text is kept per thread) */
 } fa_status;
@@ -63,16 +71,20 @@ typedef enum fa_status {
 /*
  * Arguments of one forward call. All pointers are device pointers except the struct itself.
  *
- * Layout: q is [batch, heads_q, seqlen, head_dim]; k and v are [batch, heads_kv, seqlen,
+ * Layout: q is [batch, heads_q, seqlen, head_dim]; k and v are [batch, heads_kv, seqlen_k,
  * head_dim]; o is [batch, heads_q, seqlen, head_dim]. The last (head_dim) dimension is
  * contiguous; the other three are given by the *_stride arrays, in elements, in the order
  * (batch, head, token). lse is a contiguous fp32 array [batch, heads_q, seqlen].
+ * Self-attention sets seqlen_k = seqlen.
  *
  * Packed variable-length sequences: pass cu_seqlens (device, int32, num_seqs + 1 non-decreasing
  * prefix sums with cu_seqlens[0] == 0 and cu_seqlens[num_seqs] == seqlen), batch == 1, and
- * max_seqlen >= every sequence length (it sizes the grid). Zero-length sequences are allowed.
- * libfa never reads device memory on the host, so it cannot check the cu_seqlens contents:
- * they are the caller's promise. Without cu_seqlens, num_seqs and max_seqlen are ignored.
+ * max_seqlen >= every sequence's query count (it sizes the grid). Zero-length sequences are
+ * allowed. The keys of sequence s are [cu_seqlens_k[s], cu_seqlens_k[s + 1]) of the packed
+ * K and V (cu_seqlens_k[num_seqs] == seqlen_k), or, with cu_seqlens_k NULL, the same ranges as
+ * its queries (then seqlen_k must equal seqlen). libfa never reads device memory on the host,
+ * so it cannot check the cu_seqlens contents: they are the caller's promise. Without
+ * cu_seqlens, num_seqs, max_seqlen and cu_seqlens_k are ignored.
  */
 typedef struct fa_fwd_params {
   uint32_t struct_size;   /* must equal sizeof(fa_fwd_params) (see fa_params_size) */
@@ -87,7 +99,8 @@ typedef struct fa_fwd_params {
   int32_t heads_kv;
   int32_t seqlen;         /* tokens per batch entry; total packed tokens with cu_seqlens */
   int32_t head_dim;       /* 64 or 128 */
-  int32_t causal;         /* non-zero: key j visible to query i iff j <= i */
+  int32_t causal;         /* non-zero: key j visible to query i iff
+                             j <= i + (keys - queries) of its sequence */
   float scale;            /* any finite value; 1/sqrt(head_dim) is the usual choice */
   int32_t num_seqs;
   int32_t max_seqlen;
@@ -96,6 +109,12 @@ typedef struct fa_fwd_params {
   int64_t k_stride[3];
   int64_t v_stride[3];
   int64_t o_stride[3];
+  /* since ABI version 2 */
+  int32_t seqlen_k;            /* key/value tokens per batch entry (total packed keys with
+                                  cu_seqlens_k); may be 0: then every query sees no key and
+                                  k, v may be NULL */
+  int32_t reserved0;           /* must be 0 */
+  const int32_t* cu_seqlens_k; /* packed key ranges, or NULL (see above) */
 } fa_fwd_params;
 
 /* FA_ABI_VERSION of the built library. */

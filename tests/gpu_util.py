@@ -29,23 +29,30 @@ def run(inp: si.Inputs, device="cuda", max_seqlen=None):
     q = upload(inp.q, inp.dtype, device)
     k = upload(inp.k, inp.dtype, device)
     v = upload(inp.v, inp.dtype, device)
-    cu = None
+    cu = cu_k = None
     if inp.cu_seqlens is not None:
         cu = torch.from_numpy(inp.cu_seqlens).to(device)
         if max_seqlen is None:
             max_seqlen = int(np.diff(inp.cu_seqlens).max()) if len(inp.cu_seqlens) > 1 else 0
+    if inp.cu_seqlens_k is not None:
+        cu_k = torch.from_numpy(inp.cu_seqlens_k).to(device)
     o, lse = fa.attention(q, k, v, scale=inp.scale, causal=inp.causal, cu_seqlens=cu,
-                          max_seqlen=max_seqlen)
+                          max_seqlen=max_seqlen, cu_seqlens_k=cu_k)
     torch.cuda.synchronize()
     return si.bits_to_f64(download_bits(o), inp.dtype), lse.cpu().numpy().astype(np.float64)
 
 
 def errors(o, lse, o_ref, lse_ref):
-    """(max |dO|, max LSE error) over the rows given (NaN anywhere counts as infinite)."""
-    if not (np.isfinite(o).all() and np.isfinite(lse).all()):
+    """(max |dO|, max LSE error) over the rows given (NaN anywhere counts as infinite). Rows
+    that see no key must match exactly: O = 0 and LSE = -inf on both sides."""
+    if not np.isfinite(o).all() or np.isnan(lse).any():
+        return float("inf"), float("inf")
+    empty = np.isneginf(lse_ref)
+    if not np.array_equal(np.isneginf(lse), empty) or np.isposinf(lse).any():
         return float("inf"), float("inf")
     do = float(np.abs(o - o_ref).max()) if o.size else 0.0
-    dl = float((np.abs(lse - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max()) if lse.size else 0.0
+    lf, lr = lse[~empty], lse_ref[~empty]
+    dl = float((np.abs(lf - lr) / np.maximum(np.abs(lr), 1.0)).max()) if lf.size else 0.0
     return do, dl
 
 

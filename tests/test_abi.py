@@ -36,9 +36,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_layout():
     assert fa.fa_abi_version() == fa.FA_ABI_VERSION
-    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 192
+    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 208
     assert fa.FaFwdParams.cu_seqlens.offset == 88
     assert fa.FaFwdParams.o_stride.offset == 168
+    assert fa.FaFwdParams.seqlen_k.offset == 192
+    assert fa.FaFwdParams.cu_seqlens_k.offset == 200
 
 
 ALIGNED = 0x10000
@@ -46,8 +48,8 @@ ALIGNED = 0x10000
 
 def good(**kw):
     base = dict(dtype=fa.FA_BF16, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4,
-                lse=ALIGNED * 5, batch=2, heads_q=8, heads_kv=2, seqlen=100, head_dim=128,
-                causal=1, scale=0.125)
+                lse=ALIGNED * 5, batch=2, heads_q=8, heads_kv=2, seqlen=100, seqlen_k=100,
+                head_dim=128, causal=1, scale=0.125)
     strides = dict(q_stride=(8 * 100 * 128, 100 * 128, 128), k_stride=(2 * 100 * 128, 100 * 128, 128),
                    v_stride=(2 * 100 * 128, 100 * 128, 128), o_stride=(8 * 100 * 128, 100 * 128, 128))
     base.update(kw)
@@ -62,6 +64,10 @@ def test_valid_arguments_pass():
     assert fa.fa_check_args(good(head_dim=64, dtype=fa.FA_F16, heads_kv=8, causal=0)) == fa.FA_OK
     assert fa.fa_check_args(good(scale=0.0)) == fa.FA_OK
     assert fa.fa_check_args(good(scale=-3.0)) == fa.FA_OK
+    assert fa.fa_check_args(good(seqlen_k=4000)) == fa.FA_OK
+    assert fa.fa_check_args(good(seqlen_k=0, k=0, v=0)) == fa.FA_OK  # no keys: k, v unused
+    assert fa.fa_check_args(good(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=50,
+                                 seqlen_k=700, cu_seqlens_k=ALIGNED * 7)) == fa.FA_OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,6 +93,16 @@ def test_valid_arguments_pass():
     (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=101), fa.FA_ERR_VARLEN),
     (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=0), fa.FA_ERR_VARLEN),
     (dict(batch=2 ** 20, heads_q=2 ** 10, heads_kv=2 ** 10, seqlen=2 ** 20), fa.FA_ERR_SHAPE),
+    (dict(seqlen_k=-1), fa.FA_ERR_SHAPE),
+    (dict(reserved0=1), fa.FA_ERR_SHAPE),
+    (dict(k=0), fa.FA_ERR_NULL),
+    (dict(cu_seqlens_k=ALIGNED * 7), fa.FA_ERR_VARLEN),  # key ranges without query ranges
+    (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=50, seqlen_k=700),
+     fa.FA_ERR_VARLEN),                                  # packed keys of another total length
+    (dict(seqlen_k=7, k_stride=(0, 0, 64)), fa.FA_ERR_ALIGN),  # overlapping key rows
+    (dict(batch=2 ** 10, heads_kv=2 ** 21 - 1, heads_q=2 ** 21 - 1, seqlen=1, seqlen_k=2 ** 31 - 1),
+     fa.FA_ERR_SHAPE),                                   # K/V element count
+    (dict(batch=2 ** 30, heads_q=2 ** 30, heads_kv=2 ** 30, seqlen=2 ** 30), fa.FA_ERR_SHAPE),
 ])
 def test_each_error_is_reported_before_any_device_call(kw, status):
     p = good(**kw)

@@ -28,7 +28,8 @@ def _gpu():
 
 def _oracle(inp: si.Inputs):
     q, k, v = inp.f64()
-    return oracle.attention(q, k, v, inp.scale, inp.causal, cu_seqlens=inp.cu_seqlens)
+    return oracle.attention(q, k, v, inp.scale, inp.causal, cu_seqlens=inp.cu_seqlens,
+                            cu_seqlens_k=inp.cu_seqlens_k)
 
 
 SMALL_N = [1, 2, 3, 63, 64, 65, 127, 128, 129, 200, 257, 520]
@@ -78,6 +79,34 @@ def test_kv_heads_dealt_over_xcds(hq, hkv, lens, causal):
     o, lse = run(inp)
     o_ref, lse_ref = _oracle(inp)
     assert_close(o, lse, o_ref, lse_ref, si.F16, f"heads {hq}/{hkv} lens={lens}")
+
+
+# Query chunks against key/value contexts of another length (chunked prefill, KV cache).
+CHUNK_CASES = [(1, 300), (64, 192), (100, 1000), (257, 520), (200, 200), (300, 100), (65, 1),
+               (40, 0)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d", [(si.F16, 64), (si.BF16, 128)])
+@pytest.mark.parametrize("nq,nk", CHUNK_CASES)
+def test_query_chunk_against_other_key_length(nq, nk, dtype, d, causal):
+    inp = si.random_inputs(2, 4, 2, nq, d, dtype, seed=3 * nq + nk + d, causal=causal,
+                           seqlen_k=nk)
+    o, lse = run(inp)
+    o_ref, lse_ref = _oracle(inp)
+    assert_close(o, lse, o_ref, lse_ref, dtype, f"nq={nq} nk={nk} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype,d,hq,hkv", [(si.BF16, 128, 4, 2), (si.F16, 64, 16, 8)])
+def test_packed_chunks_with_their_own_key_ranges(dtype, d, hq, hkv, causal):
+    lens_q = (0, 1, 127, 64, 5, 300, 2, 3)
+    lens_k = (3, 1, 300, 64, 0, 300, 700, 1)
+    inp = si.random_inputs(1, hq, hkv, sum(lens_q), d, dtype, seed=91, causal=causal,
+                           seq_lens=lens_q, seqlen_k=sum(lens_k), seq_lens_k=lens_k)
+    o, lse = run(inp)
+    o_ref, lse_ref = _oracle(inp)
+    assert_close(o, lse, o_ref, lse_ref, dtype, "packed chunks")
 
 
 def test_packed_with_larger_max_seqlen_bound():
@@ -236,6 +265,7 @@ def test_workload_full_size(name):
     cu = torch.from_numpy(inp.cu_seqlens).cuda() if w.varlen else None
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, cu_seqlens=cu,
                           max_seqlen=w.max_seqlen() if w.varlen else None)
+    assert w.seqlen_k is None or k.shape[2] == w.seqlen_k
     torch.cuda.synchronize()
     o_bits = download_bits(o)
     lse = lse.cpu().numpy().astype(np.float64)
