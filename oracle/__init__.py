@@ -18,6 +18,9 @@ What it computes, with the passages it follows:
   pin the definition against the pages' claim that tiling is exact.
 * ``scalar``: pure-Python (math.fsum) brute force and the two-pass online normaliser of the xspy
   page's section 3, for tiny inputs.
+* ``attention_backward``: the exact gradients dQ, dK, dV of the definition (the chain rule through
+  the materialised softmax), which the recomputing backward pass of the notes' Pitfall 3 and
+  the FromZero2AI page's mechanism 3 must reproduce.
 
 Every function here is pinned by tests under ``-m "not gpu"`` (worked examples, closed forms,
 invariants, a library routine, brute force); none is "parity unpinned".
@@ -25,6 +28,7 @@ invariants, a library routine, brute force); none is "parity unpinned".
 from .definition import (attention, attention_rows, kv_head, score_matrix_bytes,
                         softmax_rows_with_lse)
 from .online import flash_forward, merge
+from .backward import attention_backward, output_gradient_rowsum, softmax_jacobian_product
 from . import scalar
 
 __all__ = [
@@ -36,4 +40,7 @@ __all__ = [
     "flash_forward",
     "merge",
     "scalar",
+    "attention_backward",
+    "output_gradient_rowsum",
+    "softmax_jacobian_product",
 ]
