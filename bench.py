@@ -30,7 +30,8 @@ import seeded_inputs as si  # noqa: E402
 METRIC = "attention fwd TFLOP/s and % of MFMA peak, N=16K d=128 causal bf16"
 # MI355X published dense matrix peaks (TFLOP/s), per input type
 MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0}
-KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip"]
+KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip",
+                  "exact_tiled_attention_39_amd/csrc/fa_device.h"]
 
 
 def kernel_source_hash() -> str:

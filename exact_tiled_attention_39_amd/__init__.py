@@ -6,8 +6,10 @@ raises ``FaError`` on any non-OK status. There is no fallback: if the library is
 import of the binding functions raises.
 
 The C entry points (include/fa.h) are mirrored with the same names:
-``fa_fwd``, ``fa_check_args``, ``fa_status_string``, ``fa_abi_version``, ``fa_params_size``.
-``attention`` is a convenience wrapper that allocates O and LSE and calls ``fa_fwd``.
+``fa_fwd``, ``fa_check_args``, ``fa_bwd``, ``fa_bwd_check_args``, ``fa_status_string``,
+``fa_abi_version``, ``fa_params_size``, ``fa_bwd_params_size``. ``attention`` allocates O and
+LSE and calls ``fa_fwd``; ``attention_backward`` allocates dQ, dK, dV and the delta workspace
+and calls ``fa_bwd``.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 FA_F16, FA_BF16 = 0, 1
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 2
+FA_ABI_VERSION = 3
 
 _I64x3 = ctypes.c_int64 * 3
 
@@ -62,6 +64,47 @@ class FaFwdParams(ctypes.Structure):
         super().__init__(struct_size=ctypes.sizeof(FaFwdParams), **kw)
 
 
+class FaBwdParams(ctypes.Structure):
+    """Mirror of ``fa_bwd_params`` in include/fa.h (same field order and types)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("delta", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("num_seqs", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("q_stride", _I64x3),
+        ("k_stride", _I64x3),
+        ("v_stride", _I64x3),
+        ("o_stride", _I64x3),
+        ("do_stride", _I64x3),
+        ("dq_stride", _I64x3),
+        ("dk_stride", _I64x3),
+        ("dv_stride", _I64x3),
+    ]
+
+    def __init__(self, **kw):
+        super().__init__(struct_size=ctypes.sizeof(FaBwdParams), **kw)
+
+
 class FaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"libfa status {status}: {message}")
@@ -91,10 +134,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int32]
+    lib.fa_bwd_params_size.restype = ctypes.c_uint32
+    lib.fa_bwd_params_size.argtypes = []
+    lib.fa_bwd_check_args.restype = ctypes.c_int32
+    lib.fa_bwd_check_args.argtypes = [ctypes.POINTER(FaBwdParams)]
+    lib.fa_bwd.restype = ctypes.c_int32
+    lib.fa_bwd.argtypes = [ctypes.POINTER(FaBwdParams), ctypes.c_void_p]
     if lib.fa_abi_version() != FA_ABI_VERSION:
         raise ImportError(f"libfa ABI {lib.fa_abi_version()} != binding ABI {FA_ABI_VERSION}")
     if lib.fa_params_size() != ctypes.sizeof(FaFwdParams):
         raise ImportError("fa_fwd_params layout differs between libfa and the binding")
+    if lib.fa_bwd_params_size() != ctypes.sizeof(FaBwdParams):
+        raise ImportError("fa_bwd_params layout differs between libfa and the binding")
     if path is None:
         _lib = lib
     return lib
@@ -115,6 +166,15 @@ def fa_status_string(status: int) -> str:
 def fa_check_args(params: FaFwdParams) -> int:
     """Host-only validation of a filled FaFwdParams; returns the fa_status code."""
     return int(load_library().fa_check_args(ctypes.byref(params)))
+
+
+def fa_bwd_params_size() -> int:
+    return int(load_library().fa_bwd_params_size())
+
+
+def fa_bwd_check_args(params: FaBwdParams) -> int:
+    """Host-only validation of a filled FaBwdParams; returns the fa_status code."""
+    return int(load_library().fa_bwd_check_args(ctypes.byref(params)))
 
 
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -218,9 +278,89 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return o, lse
 
 
+def make_bwd_params(q, k, v, o, dout, lse, dq, dk, dv, delta, scale: float, causal: bool,
+                    cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int]) -> FaBwdParams:
+    """Fills FaBwdParams from [B, H, N, d] tensors (strides in elements)."""
+    ts = dict(q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    for name, t in ts.items():
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [batch, heads, tokens, head_dim]")
+        if t.dtype != q.dtype or q.dtype not in _DTYPES:
+            raise ValueError("q, k, v, o, dout, dq, dk, dv must share one dtype: fp16 or bf16")
+        if t.stride(3) != 1 and t.shape[3] > 1 and t.numel() > 0:
+            raise ValueError(f"{name}: the head_dim dimension must be contiguous")
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    for name in ("k", "v", "dk", "dv"):
+        if tuple(ts[name].shape) != (b, hkv, n, d):
+            raise ValueError(f"{name} must be [batch, heads_kv, tokens, head_dim] matching q")
+    for name in ("o", "dout", "dq"):
+        if tuple(ts[name].shape) != tuple(q.shape):
+            raise ValueError(f"{name} must match q")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (b, hq, n):
+            raise ValueError(f"{name} must be a contiguous float32 tensor [batch, heads_q, tokens]")
+    p = FaBwdParams(
+        dtype=_DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
+        dout=dout.data_ptr(), lse=lse.data_ptr(), delta=delta.data_ptr(), dq=dq.data_ptr(),
+        dk=dk.data_ptr(), dv=dv.data_ptr(), batch=b, heads_q=hq, heads_kv=hkv, seqlen=n,
+        head_dim=d, causal=int(bool(causal)), scale=float(scale),
+        q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o),
+        do_stride=_strides(dout), dq_stride=_strides(dq), dk_stride=_strides(dk),
+        dv_stride=_strides(dv))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        if cu_seqlens.device != q.device:
+            raise ValueError("cu_seqlens must live on the same device as q")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        p.cu_seqlens = cu_seqlens.data_ptr()
+        p.num_seqs = cu_seqlens.numel() - 1
+        p.max_seqlen = int(max_seqlen)
+    return p
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, *, scale: float, causal: bool = False,
+           cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueues the backward pass writing delta, dq, dk and dv (default: torch's stream)."""
+    lib = load_library()
+    for t in (q, k, v, o, dout, lse, dq, dk, dv, delta):
+        if not t.is_cuda:
+            raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
+    p = make_bwd_params(q, k, v, o, dout, lse, dq, dk, dv, delta, scale, causal, cu_seqlens,
+                        max_seqlen)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = int(lib.fa_bwd(ctypes.byref(p), ctypes.c_void_p(s.cuda_stream)))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+
+
+def attention_backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None,
+                       causal: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
+                       max_seqlen: Optional[int] = None):
+    """(dq, dk, dv) of sum(O * dout) for O, lse = attention(q, k, v, ...) with the same
+    arguments. Allocates the gradients and the fp32 delta workspace with torch."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if cu_seqlens is not None and max_seqlen is None:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+        max_seqlen = int(lens.max()) if lens.numel() else 0
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, scale=scale, causal=causal,
+           cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
+    return dq, dk, dv
+
+
 __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGN", "FA_ERR_GQA",
     "FA_ERR_VARLEN", "FA_ERR_ABI", "FA_ERR_LAUNCH", "FA_F16", "FA_BF16", "FaError",
     "FaFwdParams", "attention", "fa_abi_version", "fa_check_args", "fa_fwd", "fa_params_size",
-    "fa_status_string", "load_library", "make_params",
+    "fa_status_string", "load_library", "make_params", "FaBwdParams", "attention_backward",
+    "fa_bwd", "fa_bwd_check_args", "fa_bwd_params_size", "make_bwd_params",
 ]

@@ -18,7 +18,7 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "libfa.so"
 
 ARCH = "gfx950"
-SOURCES = ["fa_fwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

@@ -89,6 +89,53 @@ fa_status fa_fwd(const fa_fwd_params* p, void* stream) {
   return ls;
 }
 
+uint32_t fa_bwd_params_size(void) { return static_cast<uint32_t>(sizeof(fa_bwd_params)); }
+
+fa_status fa_bwd_check_args(const fa_bwd_params* p) {
+  if (p == nullptr) return FA_ERR_NULL;
+  if (p->struct_size != sizeof(fa_bwd_params)) return FA_ERR_ABI;
+  if (p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(p->scale)) return FA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seqlen < 0 || p->reserved0 != 0)
+    return FA_ERR_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return FA_ERR_GQA;
+  if (p->cu_seqlens != nullptr) {
+    if (p->batch != 1 || p->num_seqs < 1) return FA_ERR_VARLEN;
+    if (p->max_seqlen < 0 || p->max_seqlen > p->seqlen) return FA_ERR_VARLEN;
+    if (p->seqlen > 0 && p->max_seqlen < 1) return FA_ERR_VARLEN;
+  }
+  if (p->seqlen == 0) return FA_OK;
+  const void* ptrs[] = {p->q, p->k, p->v, p->o, p->dout, p->dq, p->dk, p->dv};
+  for (const void* t : ptrs) {
+    if (t == nullptr) return FA_ERR_NULL;
+    if (!aligned16(t)) return FA_ERR_ALIGN;
+  }
+  if (!p->lse || !p->delta) return FA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) || (reinterpret_cast<uintptr_t>(p->delta) & 3u))
+    return FA_ERR_ALIGN;
+  const int64_t* strides[] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride,
+                              p->do_stride, p->dq_stride, p->dk_stride, p->dv_stride};
+  for (const int64_t* st : strides)
+    if (!stride_ok(st, p->head_dim, p->seqlen)) return FA_ERR_ALIGN;
+  const int64_t rows = p->cu_seqlens ? p->max_seqlen : p->seqlen;
+  const int64_t groups = p->cu_seqlens ? p->num_seqs : p->batch;
+  if (product_exceeds((rows + 127) / 128, p->heads_q, groups, INT32_MAX)) return FA_ERR_SHAPE;
+  if (product_exceeds(p->batch, p->heads_q, p->seqlen, INT32_MAX - 16)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa_status fa_bwd(const fa_bwd_params* p, void* stream) {
+  const fa_status st = fa_bwd_check_args(p);
+  if (st != FA_OK) return st;
+  if (p->seqlen == 0) return FA_OK;
+  if (p->cu_seqlens != nullptr && p->max_seqlen == 0) return FA_OK;
+  const char* err = nullptr;
+  const fa_status ls = fa::launch_backward(*p, stream, &err);
+  if (ls != FA_OK && err != nullptr) g_last_hip_error = err;
+  return ls;
+}
+
 const char* fa_status_string(int32_t status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

@@ -45,23 +45,13 @@
 #include <utility>
 
 #include "fa.h"
+#include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __fp16 f16x4_tr __attribute__((__vector_size__(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_PTR(T) __attribute__((address_space(3))) T*
+using namespace dev;
 
 constexpr int kBlockM = 256;  // query rows per workgroup (B_r): 8 waves x 32 rows
 constexpr int kBlockN = 64;   // keys per K/V tile (B_c)
@@ -92,39 +82,6 @@ struct KernelArgs {
                       // XCD; 2: kv heads dealt to the 8 XCDs in turn (heads_kv % 8 == 0)
 };
 
-template <bool BF16>
-struct Elem;
-
-template <>
-struct Elem<true> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ u32x2 read_tr(const unsigned char* lds) {
-    bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_PTR(bf16x4))(lds));
-    return __builtin_bit_cast(u32x2, r);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-  }
-};
-
-template <>
-struct Elem<false> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ u32x2 read_tr(const unsigned char* lds) {
-    f16x4_tr r = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_PTR(f16x4_tr))(lds));
-    return __builtin_bit_cast(u32x2, r);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
-  }
-};
-
 // Fragment-major tile geometry. A K tile is kKBlocks blocks of 1 KB, block (kb, s) holding
 // the A operand of the S^T MFMA for key half kb and k-step s in lane order (lane L: 16 bytes
 // of key row 32 kb + L % 32, head-dims 16 s + 8 (L / 32) .. + 7). A V tile is kVBlocks blocks,
@@ -144,42 +101,6 @@ struct Geo {
   static_assert(kKBlocks == kVBlocks, "K and V tiles have the same size");
 };
 
-// Raw buffer descriptor over [base, base + bytes) in scalar registers: loads past the end
-// return zeros. (base and bytes are wave-uniform.)
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(uint32_t(a));
-  r[1] = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xFFFFu);
-  r[2] = __builtin_amdgcn_readfirstlane(uint32_t(bytes));
-  r[3] = 0x00020000u;
-  return r;
-}
-
-// One 16-byte-per-lane direct-to-LDS load: lane L's 16 bytes at byte offset voff of the
-// buffer land at LDS byte lds_addr + 16 L. Written as one asm statement so that the compiler's
-// memory-counter bookkeeping does not treat every later LDS read as dependent on it; the
-// kernel waits for these loads explicitly (wait_vmcnt) before the barrier that publishes them.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, int voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
-}
-
-// s_waitcnt on outstanding vector-memory operations only (lgkm and exp counters left at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int N>
-using Int = std::integral_constant<int, N>;
-
 // A tile is rescaled (its maximum formed) only when some lane's sum of exp2 exceeds this.
 constexpr float kLazyBound = 32768.0f;
 
@@ -197,8 +118,7 @@ void fa_fwd_kernel(const KernelArgs p) {
   unsigned char* const lds_k = smem;                          // stage s at s * kKBytes
   unsigned char* const lds_v = smem + kStages * G::kKBytes;   // stage s at s * kVBytes
   // LDS byte address of smem (the value M0 takes for a direct-to-LDS load into it)
-  const uint32_t lds_ring = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_PTR(unsigned char))(smem))));
+  const uint32_t lds_ring = lds_address(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -303,19 +223,10 @@ void fa_fwd_kernel(const KernelArgs p) {
   for (int i = 0; i < kDma; ++i) {
     const int blk = gw * kDma + i;
     int row, col;
-    if (grp == 0) {
-      // K block (kb, s): key 32 kb + L % 32, head-dims 16 s + 8 (L / 32) .. + 7
-      const int kb = blk / kSteps, s = blk % kSteps;
-      row = 32 * kb + (lane & 31);
-      col = 16 * s + 8 * (lane >> 5);
-    } else {
-      // V block (kb, tt, j): lanes 2m, 2m + 1 of the transposing read of keys part * 8 .. + 7
-      const int kbtt = blk / kOBlocks, j = blk % kOBlocks;
-      const int part = lane >> 5;
-      const int m = 2 * (lane & 31);
-      row = 16 * kbtt + 8 * part + 4 * (m >> 5) + ((m & 15) >> 2);
-      col = 32 * j + 16 * ((m >> 4) & 1) + 4 * (m & 3);
-    }
+    if (grp == 0)
+      OperandLayout::row_col(blk, lane, kSteps, row, col);  // K block (kb, s)
+    else
+      TransposeLayout::row_col(blk, lane, kOBlocks, row, col);  // V block (kb, tt, j)
     ld_voff[i] = int(row * ld_sn * 2) + col * 2;
   }
   // issue the loads of tile `tile` into ring stage ST of this group's tensor

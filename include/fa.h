@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -117,6 +117,60 @@ typedef struct fa_fwd_params {
   const int32_t* cu_seqlens_k; /* packed key ranges, or NULL (see above) */
 } fa_fwd_params;
 
+/*
+ * Arguments of one backward call: the gradients dQ, dK, dV of the loss sum(O * dO) for the
+ * forward pass above (self-attention: keys and queries of one length per sequence). The
+ * backward recomputes S and P tile by tile from Q, K and the forward's LSE instead of storing
+ * them ("Flash Attention" notes, Common Pitfalls, Pitfall 3; FromZero2AI page, "Core
+ * Mechanisms", mechanism 3):
+ *
+ *     P = exp(scale Q K^T - LSE) on visible entries, D = rowsum(dO * O),
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ *
+ * with the contributions of the query heads that share a key/value head summed.
+ *
+ * Layouts are those of fa_fwd_params: q, o, dout, dq are [batch, heads_q, seqlen, head_dim];
+ * k, v, dk, dv are [batch, heads_kv, seqlen, head_dim]; head_dim contiguous, the other strides
+ * in elements. lse is fa_fwd's output for the same q, k, v, scale and mask (contiguous fp32
+ * [batch, heads_q, seqlen]). delta is a caller-owned contiguous fp32 workspace of the same
+ * shape that fa_bwd overwrites with D (libfa allocates nothing). dq, dk, dv are written in full
+ * for every valid token, rounded to the input type from fp32 accumulators. Calls that may run
+ * at the same time need their own delta buffers.
+ */
+typedef struct fa_bwd_params {
+  uint32_t struct_size;   /* must equal sizeof(fa_bwd_params) (see fa_bwd_params_size) */
+  int32_t dtype;          /* fa_dtype */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;          /* fa_fwd's output */
+  const void* dout;       /* dL/dO */
+  const float* lse;       /* fa_fwd's log-sum-exp */
+  float* delta;           /* workspace, written */
+  void* dq;
+  void* dk;
+  void* dv;
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t seqlen;
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t causal;         /* non-zero: key j visible to query i iff j <= i */
+  float scale;
+  int32_t num_seqs;
+  int32_t max_seqlen;
+  int32_t reserved0;      /* must be 0 */
+  const int32_t* cu_seqlens; /* NULL for fixed-length batches */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t do_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+} fa_bwd_params;
+
 /* FA_ABI_VERSION of the built library. */
 int32_t fa_abi_version(void);
 
@@ -133,6 +187,18 @@ fa_status fa_check_args(const fa_fwd_params* p);
  * caller's next synchronisation of the stream. NaN or Inf inputs are not checked and propagate.
  */
 fa_status fa_fwd(const fa_fwd_params* p, void* stream);
+
+/* sizeof(fa_bwd_params) as compiled into the library. */
+uint32_t fa_bwd_params_size(void);
+
+/* Host-only argument validation of a backward call (no device call). */
+fa_status fa_bwd_check_args(const fa_bwd_params* p);
+
+/*
+ * Enqueue the backward pass on `stream`: writes delta, then dK and dV, then dQ. Argument
+ * errors are returned before any device call; seqlen == 0 is a no-op returning FA_OK.
+ */
+fa_status fa_bwd(const fa_bwd_params* p, void* stream);
 
 /* Static text for a status code; for FA_ERR_LAUNCH, the HIP error of this thread's last
  * failed launch. Never NULL. */

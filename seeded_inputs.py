@@ -211,6 +211,12 @@ def random_inputs(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim
                   dtype, 1.0 / math.sqrt(head_dim) if scale is None else scale, causal, cu, cu_k)
 
 
+def random_output_grad(inp: Inputs, seed: int) -> np.ndarray:
+    """dL/dO for a backward check: N(0, 1) rounded to the dtype, shaped like Q (bit patterns)."""
+    rng = np.random.default_rng(seed)
+    return round_to_bits(rng.standard_normal(inp.q.shape, dtype=np.float32), inp.dtype)
+
+
 def workload_inputs(w: Workload) -> Inputs:
     """The seeded inputs of a named workload (the varlen lengths are part of the workload)."""
     return random_inputs(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, w.dtype, w.seed,

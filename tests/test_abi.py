@@ -20,7 +20,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_abi_version", "fa_check_args", "fa_fwd",
+    assert declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_check_args",
+                                    "fa_bwd_params_size", "fa_check_args", "fa_fwd",
                                     "fa_params_size", "fa_status_string"]
 
 
@@ -100,7 +101,8 @@ def test_valid_arguments_pass():
     (dict(batch=1, cu_seqlens=ALIGNED * 6, num_seqs=3, max_seqlen=50, seqlen_k=700),
      fa.FA_ERR_VARLEN),                                  # packed keys of another total length
     (dict(seqlen_k=7, k_stride=(0, 0, 64)), fa.FA_ERR_ALIGN),  # overlapping key rows
-    (dict(batch=2 ** 10, heads_kv=2 ** 21 - 1, heads_q=2 ** 21 - 1, seqlen=1, seqlen_k=2 ** 31 - 1),
+    (dict(batch=2 ** 10, heads_kv=2 ** 21 - 1, heads_q=2 ** 21 - 1, seqlen=1,
+          seqlen_k=2 ** 31 - 1),
      fa.FA_ERR_SHAPE),                                   # K/V element count
     (dict(batch=2 ** 30, heads_q=2 ** 30, heads_kv=2 ** 30, seqlen=2 ** 30), fa.FA_ERR_SHAPE),
 ])
@@ -147,3 +149,51 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     assert (p.batch, p.heads_q, p.heads_kv, p.seqlen, p.head_dim, p.causal) == (1, 2, 2, 8, 64, 1)
     assert list(p.q_stride) == [1024, 512, 64]
     assert fa.fa_check_args(p) == fa.FA_OK
+
+
+def good_bwd(**kw):
+    ptrs = dict(q=1, k=2, v=3, o=4, dout=5, lse=6, delta=7, dq=8, dk=9, dv=10)
+    base = {name: ALIGNED * i for name, i in ptrs.items()}
+    base.update(dtype=fa.FA_BF16, batch=2, heads_q=8, heads_kv=2, seqlen=100, head_dim=128,
+                causal=1, scale=0.125)
+    base.update({k: v for k, v in kw.items() if not k.endswith("_stride")})
+    p = fa.FaBwdParams(**base)
+    qs, ks = (8 * 100 * 128, 100 * 128, 128), (2 * 100 * 128, 100 * 128, 128)
+    for name, val in (("q", qs), ("k", ks), ("v", ks), ("o", qs), ("do", qs), ("dq", qs),
+                      ("dk", ks), ("dv", ks)):
+        setattr(p, name + "_stride", fa._I64x3(*kw.get(name + "_stride", val)))
+    return p
+
+
+def test_backward_struct_layout_and_valid_arguments():
+    assert fa.fa_bwd_params_size() == ctypes.sizeof(fa.FaBwdParams) == 328
+    assert fa.FaBwdParams.cu_seqlens.offset == 128
+    assert fa.fa_bwd_check_args(good_bwd()) == fa.FA_OK
+    assert fa.fa_bwd_check_args(good_bwd(head_dim=64, dtype=fa.FA_F16, causal=0)) == fa.FA_OK
+    assert fa.fa_bwd_check_args(good_bwd(batch=1, cu_seqlens=ALIGNED * 11, num_seqs=4,
+                                         max_seqlen=40)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(delta=0), fa.FA_ERR_NULL),
+    (dict(dout=0), fa.FA_ERR_NULL),
+    (dict(dk=ALIGNED + 8), fa.FA_ERR_ALIGN),
+    (dict(delta=ALIGNED + 2), fa.FA_ERR_ALIGN),
+    (dict(do_stride=(0, 0, 132)), fa.FA_ERR_ALIGN),
+    (dict(dq_stride=(0, 0, 64)), fa.FA_ERR_ALIGN),
+    (dict(head_dim=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_UNSUPPORTED),
+    (dict(heads_kv=3), fa.FA_ERR_GQA),
+    (dict(reserved0=1), fa.FA_ERR_SHAPE),
+    (dict(cu_seqlens=ALIGNED * 11, num_seqs=3, max_seqlen=50), fa.FA_ERR_VARLEN),  # batch 2
+    (dict(batch=2 ** 16, heads_q=2 ** 10, heads_kv=2 ** 10, seqlen=2 ** 10), fa.FA_ERR_SHAPE),
+])
+def test_backward_errors_before_any_device_call(kw, status):
+    p = good_bwd(**kw)
+    assert fa.fa_bwd_check_args(p) == status
+    assert fa.load_library().fa_bwd(ctypes.byref(p), None) == status
+
+
+def test_backward_empty_problem_is_a_no_op():
+    p = good_bwd(seqlen=0, q=0, k=0, v=0, o=0, dout=0, lse=0, delta=0, dq=0, dk=0, dv=0)
+    assert fa.load_library().fa_bwd(ctypes.byref(p), None) == fa.FA_OK
