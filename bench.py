@@ -113,6 +113,96 @@ def copy_calibration(torch, mib: int) -> int:
     return 0
 
 
+def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up) -> int:
+    """The backward pass (delta, dK/dV and dQ kernels) of a self-attention workload."""
+    import oracle
+
+    if w.seqlen_k is not None:
+        print("the backward pass covers self-attention workloads only", file=sys.stderr)
+        return 2
+    dev = q.device
+    dout_bits = si.random_output_grad(inp, seed=w.seed + 100)
+    do = up(dout_bits)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
+    max_seqlen = w.max_seqlen() if w.varlen else None
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, cu_seqlens=cu,
+                          max_seqlen=max_seqlen)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, scale=w.scale, causal=w.causal,
+                  cu_seqlens=cu, max_seqlen=max_seqlen)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops = 2.5 * w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_ms = float(np.mean(launch_ms))
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+
+    # sampled dQ rows against the oracle (each dQ row depends on its own row only)
+    rows = si.sample_rows(w, 0.0, seed=8, max_rows=32)
+    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    dof = si.bits_to_f64(dout_bits, w.dtype).astype(np.float32)
+    dq_ref = oracle.attention_backward_dq_rows(qf, kf, vf, dof, w.scale, w.causal, rows,
+                                               cu_seqlens=inp.cu_seqlens)
+    idx = tuple(np.array(rows).T)
+    dq_gpu = si.bits_to_f64(dq.view(torch.int16).cpu().numpy().view(np.uint16)[idx], w.dtype)
+    line = {
+        "metric": f"attention bwd TFLOP/s and % of MFMA peak, {w.name}",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and output gradient, see seeded_inputs.py)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+            "seqlen": w.seqlen, "head_dim": w.head_dim, "causal": w.causal,
+            "flop_count": flops,
+            "flop_convention": ("2.5 x the forward's convention: 5 products (S, dP, dV, dK, dQ); "
+                                "the kernels run 7 (S and dP again for dQ)"),
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (avg_ms * 1e-3) / 1e12 / peak, 4),
+            "traffic": None,
+            "kernel": "fa_bwd (fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, fa_bwd_dq_kernel)",
+            "avg_launch_ms": round(avg_ms, 4),
+            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        },
+        "parity": {"dq_rows": len(rows),
+                   "max_abs_ddQ": float(np.abs(dq_gpu - dq_ref).max()),
+                   "max_abs_dQ_ref": float(np.abs(dq_ref).max())},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +211,8 @@ def main() -> int:
     ap.add_argument("--workload", default=si.HEADLINE, choices=si.WORKLOAD_ORDER)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (fa_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 launches), the "
                          "known-size reference that scales the HBM byte counters")
@@ -151,6 +243,8 @@ def main() -> int:
         return torch.from_numpy(bits.view(np.int16)).view(tdt).to(dev)
 
     q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    if args.backward:
+        return bench_backward(args, torch, fa, w, inp, q, k, v, up)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None

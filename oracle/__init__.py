@@ -28,7 +28,8 @@ invariants, a library routine, brute force); none is "parity unpinned".
 from .definition import (attention, attention_rows, kv_head, score_matrix_bytes,
                         softmax_rows_with_lse)
 from .online import flash_forward, merge
-from .backward import attention_backward, output_gradient_rowsum, softmax_jacobian_product
+from .backward import (attention_backward, attention_backward_dq_rows, output_gradient_rowsum,
+                       softmax_jacobian_product)
 from . import scalar
 
 __all__ = [
@@ -41,6 +42,7 @@ __all__ = [
     "merge",
     "scalar",
     "attention_backward",
+    "attention_backward_dq_rows",
     "output_gradient_rowsum",
     "softmax_jacobian_product",
 ]

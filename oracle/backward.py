@@ -20,6 +20,7 @@ length per sequence).
 """
 from __future__ import annotations
 
+from collections import defaultdict
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
@@ -71,3 +72,37 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 def output_gradient_rowsum(o: np.ndarray, do: np.ndarray) -> np.ndarray:
     """D_i = sum_c dO_ic O_ic, which equals sum_j P_ij dP_ij because O = P V."""
     return np.einsum("bhnd,bhnd->bhn", np.asarray(do, np.float64), np.asarray(o, np.float64))
+
+
+def attention_backward_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                               scale: float, causal: bool, rows,
+                               cu_seqlens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """dQ of selected rows (b, q_head, token) only: every term of dQ_i depends on row i alone
+    (its scores, probabilities and dP row, and D_i = sum_j P_ij dP_ij), so a row is computed
+    from q_i, do_i and the keys and values it sees. Returns [R, d] in the order of ``rows``."""
+    rows = list(rows)
+    b_, hq, n, d = q.shape
+    hkv = k.shape[1]
+    segs = _segments(n, cu_seqlens)
+    starts = np.array([a for a, _ in segs])
+    out = np.empty((len(rows), d))
+    by_head = defaultdict(list)
+    for r, (b, h, i) in enumerate(rows):
+        by_head[(b, kv_head(h, hq, hkv))].append(r)
+    for (b, hk), idx in by_head.items():
+        kh = np.asarray(k[b, hk], dtype=np.float64)
+        vh = np.asarray(v[b, hk], dtype=np.float64)
+        for r in idx:
+            _, h, i = rows[r]
+            seg = int(np.searchsorted(starts, i, side="right")) - 1
+            while segs[seg][1] <= i:
+                seg += 1
+            s0, s1 = segs[seg]
+            end = i + 1 if causal else s1
+            qi = np.asarray(q[b, h, i], dtype=np.float64)[None, :]
+            doi = np.asarray(do[b, h, i], dtype=np.float64)[None, :]
+            s = _head_scores(qi, kh[s0:end], scale)
+            p, _ = softmax_rows_with_lse(s, np.ones_like(s, dtype=bool))
+            ds = softmax_jacobian_product(p, doi @ vh[s0:end].T)
+            out[r] = scale * (ds @ kh[s0:end])[0]
+    return out

@@ -136,6 +136,17 @@ def test_packed_equals_separate_sequences(causal):
             np.testing.assert_array_equal(g[:, :, sl], w_)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_full_backward(causal):
+    lens = [9, 0, 20, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, do = _problem(1, 4, 2, sum(lens), 8, seed=10)
+    dq, _, _ = attention_backward(q, k, v, do, 0.45, causal, cu_seqlens=cu)
+    rows = [(0, h, i) for h in range(4) for i in range(sum(lens))]
+    got = ob.attention_backward_dq_rows(q, k, v, do, 0.45, causal, rows, cu_seqlens=cu)
+    np.testing.assert_allclose(got, dq.reshape(-1, 8), rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------------------------------------------------------
 # Planted mistakes
 # ------------------------------------------------------------------------------------------
