@@ -19,6 +19,11 @@ LIB = PKG / "libfa.so"
 
 ARCH = "gfx950"
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+# Per-source extra flags. The backward kernels run one wave per SIMD with more live state than
+# the 256 VALU-addressable registers: the VGPR form of every MFMA keeps S, dP and the
+# accumulators where the element-wise code reads them, and the accumulation registers then
+# serve as overflow space, instead of the default form's copies through them.
+EXTRA_FLAGS = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -47,7 +52,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> pathlib.Path:
         procs = []
         for src in SOURCES:
             obj = pathlib.Path(tmp) / (src + ".o")
-            cmd = [cc, *FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+            cmd = [cc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", str(CSRC / src), "-o", str(obj)]
             if resource_usage and src.endswith(".hip"):
                 cmd.append("-Rpass-analysis=kernel-resource-usage")
             if verbose:

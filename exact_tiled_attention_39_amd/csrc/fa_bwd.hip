@@ -40,9 +40,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kOwn = 128;        // rows a workgroup owns: 4 waves x 32
-constexpr int kTileRows = 64;    // rows of the streamed side per step
-constexpr int kBwdThreads = 256;
+constexpr int kTileRows = 32;    // rows of the streamed side per step
 
 struct BwdArgs {
   const uint16_t* q;
@@ -68,7 +66,8 @@ struct BwdArgs {
   int32_t heads_q;
   int32_t heads_kv;
   int32_t group;      // heads_q / heads_kv
-  int32_t n_blocks;   // 128-row blocks per (batch entry or sequence)
+  int32_t n_kblocks;  // 128-key blocks per (batch entry or sequence)
+  int32_t n_qblocks;  // 256-query blocks per (batch entry or sequence)
   int32_t rows_delta; // batch * heads_q * seqlen
   float c;            // |scale| * log2(e), or log2(e) when scale == 0
   uint32_t s_and;     // 0 when scale == 0, else all ones (applied to the resident operand)
@@ -108,9 +107,8 @@ template <int D>
 struct BwdGeo {
   static constexpr int kSteps = D / 16;       // head-dim steps of a contraction over D
   static constexpr int kOBlocks = D / 32;     // 32-wide head-dim blocks
-  static constexpr int kBlocks = D / 8;       // 1 KB blocks per 64-row tile per layout
+  static constexpr int kBlocks = kTileRows * D / 512;  // 1 KB blocks per tile per layout
   static constexpr int kTileBytes = kBlocks * 1024;
-  static constexpr int kPerWave = kBlocks / 4;  // blocks of one layout issued per wave
 };
 
 // Workgroup order: (batch entry or sequence, head) pairs in plain order, block index heaviest
@@ -177,30 +175,81 @@ __device__ __forceinline__ void load_resident(const uint16_t* base, int64_t sn, 
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys.
+// Both main kernels run 8 waves, two per SIMD, each wave within 256 registers, so that the
+// SIMD interleaves one wave's element-wise work with the other's matrix products. A tile of 32
+// rows of the streamed side moves through double-buffered LDS per step.
+
+constexpr int kWaves = 8;
+constexpr int kThreads8 = 64 * kWaves;
+
+// LDS operand reads of one tile for an MFMA chain over the head dimension: block s of a tile in
+// the operand layout (32 rows x 16 head-dims) at `base`.
+template <bool BF16, int kSteps>
+__device__ __forceinline__ f32x16 chain_over_d(const unsigned char* base, const u32x4* bop) {
+  using E = Elem<BF16>;
+  f32x16 acc = f32x16{};
+  u32x4 a[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) a[s] = *reinterpret_cast<const u32x4*>(base + s * 1024);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) acc = E::mfma(a[s], bop[s], acc);
+  return acc;
+}
+
+// acc[j] += (32 head-dims of block j) x (tile rows) . B, over the tile's two 16-row steps, with
+// the A operand from the transposing layout at `base` (block (t, j) at (t * kOBlocks + j) KB).
+template <bool BF16, int kOBlocks>
+__device__ __forceinline__ void chain_over_rows(const unsigned char* base, const u32x4 b[2],
+                                                f32x16* acc) {
+  using E = Elem<BF16>;
+  u32x4 a[2 * kOBlocks];
+#pragma unroll
+  for (int m = 0; m < 2 * kOBlocks; ++m) {
+    const u32x2 lo = E::read_tr(base + m * 1024);
+    const u32x2 hi = E::read_tr(base + m * 1024 + 512);
+    a[m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+#pragma unroll
+  for (int m = 0; m < 2 * kOBlocks; ++m) acc[m % kOBlocks] = E::mfma(a[m], b[m / kOBlocks],
+                                                                     acc[m % kOBlocks]);
+}
+
+__device__ __forceinline__ void tile_sync() {
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
+// each, waves 4-7 dK for the same keys; a SIMD holds one of each. Both roles form S = Q K^T and
+// P; the dK role also dP = dO V^T and dS. Splitting the roles costs S twice (5 products per
+// tile instead of 4) but keeps each wave's state within 256 registers.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
+                          amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const BwdArgs p) {
   using E = Elem<BF16>;
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  constexpr int kPer = G::kPerWave;
-  // stage: Q operand | Q transposing | dO operand | dO transposing | LSE rows | D rows
-  constexpr int kQop = 0, kQtr = G::kTileBytes, kDop = 2 * G::kTileBytes,
+  constexpr int kPer = G::kBlocks / 2;  // blocks of one layout issued per wave (two per layout)
+  // stage: Q operand | dO operand | Q transposing | dO transposing | 32 LSE | 32 D (a 1 KB
+  // direct-to-LDS load each)
+  constexpr int kQop = 0, kDop = G::kTileBytes, kQtr = 2 * G::kTileBytes,
                 kDtr = 3 * G::kTileBytes, kLse = 4 * G::kTileBytes, kDel = kLse + 1024;
-  constexpr int kStage = kDel + 1024;
+  constexpr int kStage = kLse + 2048;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2;  // 0: dV, 1: dK
   const int half = lane >> 5;
 
-  const int pairs = gridDim.x / p.n_blocks;
-  const Item it = item_of(pairs, p.heads_kv, p.n_blocks, false);
+  const int pairs = gridDim.x / p.n_kblocks;
+  const Item it = item_of(pairs, p.heads_kv, p.n_kblocks, false);
   const int hk = it.h;
   int seq0 = 0, slen = p.seqlen, bidx = it.b;
   if (VARLEN) {
@@ -208,182 +257,150 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     slen = p.cu_seqlens[it.b + 1] - seq0;
     bidx = 0;
   }
-  const int k0 = it.blk * kOwn;
+  const int k0 = it.blk * 128;
   if (k0 >= slen) return;  // uniform across the workgroup
-  const int kw0 = k0 + 32 * wave;  // first key of this wave
-  const int key = kw0 + (lane & 31);  // key of this lane (accumulator column)
+  const int kw0 = k0 + 32 * (wave & 3);  // first key of this wave
+  const int key = kw0 + (lane & 31);     // key of this lane (accumulator column)
 
-  // resident K^T and V^T operands (K scaled by the sign of the scale, or zeroed for scale 0)
-  u32x4 kf[kSteps], vf[kSteps];
-  load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0, slen,
-                   lane, kf);
-  load_resident<D>(p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn, p.v_sn, kw0, slen,
-                   lane, vf);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) kf[s] = (kf[s] & p.s_and) ^ p.s_xor;
-
-  f32x16 dkacc[kOBlocks], dvacc[kOBlocks];
-#pragma unroll
-  for (int j = 0; j < kOBlocks; ++j) dkacc[j] = dvacc[j] = f32x16{};
-
-  // query tiles: causal keys k0.. are seen by queries >= k0 only
   const int t_first = CAUSAL ? k0 / kTileRows : 0;
   const int n_qt = (slen + kTileRows - 1) / kTileRows;
   const int per_head = n_qt - t_first;
   const int n_steps = per_head * p.group;
 
-  // per-lane source offsets of this wave's DMA blocks (rows of the tile, bytes)
-  int op_off[kPer], tr_off[kPer], dop_off[kPer], dtr_off[kPer];
+  // DMA: 4 layouts x kBlocks blocks per tile over 8 waves; wave w issues blocks
+  // [kPer (w % 2), kPer (w % 2 + 1)) of layout w / 2 (Q op, dO op, Q tr, dO tr)
+  const int lay = wave >> 1;
+  int ld_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
+    const int blk = (wave & 1) * kPer + i;
     int row, col;
-    OperandLayout::row_col(wave * kPer + i, lane, kSteps, row, col);
-    op_off[i] = int(row * p.q_sn * 2) + col * 2;
-    dop_off[i] = int(row * p.do_sn * 2) + col * 2;
-    TransposeLayout::row_col(wave * kPer + i, lane, kOBlocks, row, col);
-    tr_off[i] = int(row * p.q_sn * 2) + col * 2;
-    dtr_off[i] = int(row * p.do_sn * 2) + col * 2;
+    if (lay < 2)
+      OperandLayout::row_col(blk, lane, kSteps, row, col);
+    else
+      TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
+    ld_off[i] = int(row * ((lay & 1) ? p.do_sn : p.q_sn) * 2) + col * 2;
   }
-
-  auto step_head = [&](int st) { return it.h * p.group + st / per_head; };
-  auto step_tile = [&](int st) { return t_first + st % per_head; };
-
-  // issue the loads of step st into stage ST
   auto issue = [&](auto stage, int st) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
-    const int h = step_head(st);
-    const int r0 = step_tile(st) * kTileRows;
+    const int h = it.h * p.group + st / per_head;
+    const int r0 = (t_first + st % per_head) * kTileRows;
     const int rows = min(slen - r0, kTileRows);
-    const uint16_t* qb = p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0 + r0) * p.q_sn;
-    const uint16_t* db = p.dout + bidx * p.do_sb + h * p.do_sh + int64_t(seq0 + r0) * p.do_sn;
-    const u32x4 rq = make_rsrc(qb, int((rows - 1) * p.q_sn * 2) + D * 2);
-    const u32x4 rd = make_rsrc(db, int((rows - 1) * p.do_sn * 2) + D * 2);
-    const uint32_t base = lds0 + ST * kStage + wave * kPer * 1024;
+    const bool is_do = lay & 1;
+    const uint16_t* src = is_do
+        ? p.dout + bidx * p.do_sb + h * p.do_sh + int64_t(seq0 + r0) * p.do_sn
+        : p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0 + r0) * p.q_sn;
+    const int64_t sn = is_do ? p.do_sn : p.q_sn;
+    const u32x4 rs = make_rsrc(src, int((rows - 1) * sn * 2) + D * 2);
+    const uint32_t base = lds0 + ST * kStage + lay * G::kTileBytes + (wave & 1) * kPer * 1024;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      dma16(rq, base + kQop + i * 1024, op_off[i]);
-      dma16(rq, base + kQtr + i * 1024, tr_off[i]);
-      dma16(rd, base + kDop + i * 1024, dop_off[i]);
-      dma16(rd, base + kDtr + i * 1024, dtr_off[i]);
-    }
+    for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     if (wave < 2) {
-      // 64 fp32 rows of LSE (wave 0) or D (wave 1): lanes 0..15 carry them, the rest read 0
-      const int64_t row0 = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + r0;
-      const float* src = wave == 0 ? p.lse + row0 : p.delta + row0;
-      dma16(make_rsrc(src, rows * 4), lds0 + ST * kStage + (wave == 0 ? kLse : kDel),
+      // 32 fp32 rows of LSE (wave 0) or D (wave 1): lanes 0..7 carry them, the rest read 0
+      const int64_t lrow = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + r0;
+      const float* lsrc = wave == 0 ? p.lse + lrow : p.delta + lrow;
+      dma16(make_rsrc(lsrc, rows * 4), lds0 + ST * kStage + (wave == 0 ? kLse : kDel),
             lane * 16);
     }
   };
 
-  auto compute = [&](auto stage, int st) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    const unsigned char* sb = smem + ST * kStage;
-    const int r0 = step_tile(st) * kTileRows;
-    // S = Q K^T and dP = dO V^T for the two 32-query halves of the tile
-    f32x16 sacc[2], dpacc[2];
+  // resident K^T (sign of the scale applied) for both roles, V^T for the dK role
+  u32x4 kf[kSteps];
+  load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0, slen,
+                   lane, kf);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = f32x16{};
-      dpacc[qb] = f32x16{};
+  for (int s = 0; s < kSteps; ++s) kf[s] = (kf[s] & p.s_and) ^ p.s_xor;
+
+  // one role's loop; both roles run the same barriers
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr bool DK = decltype(role_c)::value;
+    u32x4 vf[kSteps];
+    if constexpr (DK)
+      load_resident<D>(p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn, p.v_sn, kw0,
+                       slen, lane, vf);
+    f32x16 acc[kOBlocks];
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sb + kQop + (qb * kSteps + s) * 1024 +
-                                                        lane * 16);
-        sacc[qb] = E::mfma(a, kf[s], sacc[qb]);
-        const u32x4 g = *reinterpret_cast<const u32x4*>(sb + kDop + (qb * kSteps + s) * 1024 +
-                                                        lane * 16);
-        dpacc[qb] = E::mfma(g, vf[s], dpacc[qb]);
-      }
-    }
-    // P = exp2(c S - log2e L) and dS = P (dP - D); entry i of half qb is query row
-    // r0 + 32 qb + 8 (i / 4) + 4 half + i % 4
-    u32x4 pp[2][2], pds[2][2];
-    const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int j = 0; j < kOBlocks; ++j) acc[j] = f32x16{};
+
+    auto compute = [&](auto stage, int st) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage)::value;
+      const unsigned char* sb = smem + ST * kStage;
+      const int r0 = (t_first + st % per_head) * kTileRows;
+      f32x16 sacc = chain_over_d<BF16, kSteps>(sb + kQop + lane * 16, kf);
+      f32x16 dpacc;
+      if constexpr (DK) dpacc = chain_over_d<BF16, kSteps>(sb + kDop + lane * 16, vf);
+      // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
       float lse[16], del[16];
-      read_rows16(reinterpret_cast<const float*>(sb + kLse) + 32 * qb, half, lse);
-      read_rows16(reinterpret_cast<const float*>(sb + kDel) + 32 * qb, half, del);
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qrow = r0 + 32 * qb + 8 * (i >> 2) + 4 * half + (i & 3);
-        float x = fmaf(sacc[qb][i], p.c, -lse[i] * kLog2e);
-        if (edge) {
-          const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
-          x = ok ? x : -INFINITY;
-        }
-        pv[i] = __builtin_amdgcn_exp2f(x);
-        dsv[i] = pv[i] * (dpacc[qb][i] - del[i]);
-      }
+      read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
+      if constexpr (DK) read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
+      const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
+      u32x4 pb[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pp[qb][tt][e] = E::pack(pv[8 * tt + 2 * e], pv[8 * tt + 2 * e + 1]);
-          pds[qb][tt][e] = E::pack(dsv[8 * tt + 2 * e], dsv[8 * tt + 2 * e + 1]);
+        for (int w = 0; w < 4; ++w) {
+          float v2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int i = 8 * tt + 2 * w + u;
+            float x = fmaf(sacc[i], p.c, lse[i] * -kLog2e);
+            if (edge) {
+              const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+              const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
+              x = ok ? x : -INFINITY;
+            }
+            const float pr = __builtin_amdgcn_exp2f(x);
+            v2[u] = DK ? pr * (dpacc[i] - del[i]) : pr;
+          }
+          pb[tt][w] = E::pack(v2[0], v2[1]);
         }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, contracting over the tile's 64 queries
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int j = 0; j < kOBlocks; ++j) {
-          const int blk = ((2 * qb + tt) * kOBlocks + j) * 1024;
-          const u32x2 dlo = E::read_tr(sb + kDtr + blk + lane * 8);
-          const u32x2 dhi = E::read_tr(sb + kDtr + blk + 512 + lane * 8);
-          dvacc[j] = E::mfma(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, pp[qb][tt], dvacc[j]);
-          const u32x2 qlo = E::read_tr(sb + kQtr + blk + lane * 8);
-          const u32x2 qhi = E::read_tr(sb + kQtr + blk + 512 + lane * 8);
-          dkacc[j] = E::mfma(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, pds[qb][tt], dkacc[j]);
+      // dV^T += dO^T P (dV role) or dK^T += Q^T dS (dK role), over the tile's 32 queries
+      chain_over_rows<BF16, kOBlocks>(sb + (DK ? kQtr : kDtr) + lane * 8, pb, acc);
+    };
+
+    if (n_steps > 0) {
+      issue(Int<0>{}, 0);
+      tile_sync();
+      for (int st = 0; st < n_steps; st += 2) {
+        if (st + 1 < n_steps) issue(Int<1>{}, st + 1);
+        compute(Int<0>{}, st);
+        tile_sync();
+        if (st + 1 < n_steps) {
+          if (st + 2 < n_steps) issue(Int<0>{}, st + 2);
+          compute(Int<1>{}, st + 1);
+          tile_sync();
         }
-  };
-
-  auto sync = [&]() __attribute__((always_inline)) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __syncthreads();
-  };
-
-  if (n_steps > 0) {
-    issue(Int<0>{}, 0);
-    sync();
-    for (int st = 0; st < n_steps; st += 2) {
-      if (st + 1 < n_steps) issue(Int<1>{}, st + 1);
-      compute(Int<0>{}, st);
-      sync();
-      if (st + 1 < n_steps) {
-        if (st + 2 < n_steps) issue(Int<0>{}, st + 2);
-        compute(Int<1>{}, st + 1);
-        sync();
       }
     }
-  }
-
-  if (key < slen) {
-    uint16_t* dkrow = p.dk + bidx * p.dk_sb + hk * p.dk_sh + int64_t(seq0 + key) * p.dk_sn;
-    uint16_t* dvrow = p.dv + bidx * p.dv_sb + hk * p.dv_sh + int64_t(seq0 + key) * p.dv_sn;
-    store_rows<D, BF16>(dkrow, dkacc, p.scale, half);
-    store_rows<D, BF16>(dvrow, dvacc, 1.f, half);
-  }
+    if (key < slen) {
+      if constexpr (DK)
+        store_rows<D, BF16>(p.dk + bidx * p.dk_sb + hk * p.dk_sh + int64_t(seq0 + key) * p.dk_sn,
+                            acc, p.scale, half);
+      else
+        store_rows<D, BF16>(p.dv + bidx * p.dv_sb + hk * p.dv_sh + int64_t(seq0 + key) * p.dv_sn,
+                            acc, 1.f, half);
+    }
+  };
+  if (role)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------------------
-// dQ: one workgroup per 128 queries.
+// dQ: one workgroup per 256 queries, 8 waves of 32 queries.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads),
-                          amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
+                          amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const BwdArgs p) {
   using E = Elem<BF16>;
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  constexpr int kPer = G::kPerWave;
-  // stage: K operand | K transposing | V operand
-  constexpr int kKop = 0, kKtr = G::kTileBytes, kVop = 2 * G::kTileBytes;
+  // stage: K operand | V operand | K transposing
+  constexpr int kKop = 0, kVop = G::kTileBytes, kKtr = 2 * G::kTileBytes;
   constexpr int kStage = 3 * G::kTileBytes;
+  constexpr int kDmaBlocks = 3 * G::kBlocks;  // per tile, spread over the 8 waves
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
   const uint32_t lds0 = lds_address(smem);
 
@@ -392,8 +409,8 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
 
-  const int pairs = gridDim.x / p.n_blocks;
-  const Item it = item_of(pairs, p.heads_q, p.n_blocks, CAUSAL);
+  const int pairs = gridDim.x / p.n_qblocks;
+  const Item it = item_of(pairs, p.heads_q, p.n_qblocks, CAUSAL);
   const int h = it.h;
   const int hk = h / p.group;
   int seq0 = 0, slen = p.seqlen, bidx = it.b;
@@ -402,12 +419,11 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
     slen = p.cu_seqlens[it.b + 1] - seq0;
     bidx = 0;
   }
-  const int q0 = it.blk * kOwn;
+  const int q0 = it.blk * 256;
   if (q0 >= slen) return;  // uniform across the workgroup
-  const int qw0 = q0 + 32 * wave;     // first query of this wave
+  const int qw0 = q0 + 32 * wave;      // first query of this wave
   const int qrow = qw0 + (lane & 31);  // query of this lane (accumulator column)
 
-  // resident Q^T (sign and zero of the scale applied) and dO^T operands
   u32x4 qf[kSteps], dof[kSteps];
   load_resident<D>(p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0) * p.q_sn, p.q_sn, qw0, slen,
                    lane, qf);
@@ -415,45 +431,49 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
                    slen, lane, dof);
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) qf[s] = (qf[s] & p.s_and) ^ p.s_xor;
-  float lse2 = 0.f, del = 0.f;
+  float nlse = 0.f, del = 0.f;  // -log2e LSE and D of this lane's query
   if (qrow < slen) {
     const int64_t r = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + qrow;
-    lse2 = p.lse[r] * kLog2e;
+    nlse = -p.lse[r] * kLog2e;
     del = p.delta[r];
   }
-
   f32x16 dqacc[kOBlocks];
 #pragma unroll
   for (int j = 0; j < kOBlocks; ++j) dqacc[j] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(slen, q0 + kOwn) : slen;
+  const int kv_end = CAUSAL ? min(slen, q0 + 256) : slen;
   const int n_tiles = (kv_end + kTileRows - 1) / kTileRows;
 
-  int op_off_k[kPer], tr_off_k[kPer], op_off_v[kPer];
+  // DMA: block b of the tile's three layouts (K op, V op, K tr) goes to wave b % 8
+  constexpr int kPerW = (kDmaBlocks + kWaves - 1) / kWaves;
+  int ld_off[kPerW];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    int row, col;
-    OperandLayout::row_col(wave * kPer + i, lane, kSteps, row, col);
-    op_off_k[i] = int(row * p.k_sn * 2) + col * 2;
-    op_off_v[i] = int(row * p.v_sn * 2) + col * 2;
-    TransposeLayout::row_col(wave * kPer + i, lane, kOBlocks, row, col);
-    tr_off_k[i] = int(row * p.k_sn * 2) + col * 2;
+  for (int i = 0; i < kPerW; ++i) {
+    const int b = i * kWaves + wave;
+    const int lay = b / G::kBlocks, blk = b % G::kBlocks;
+    int row = 0, col = 0;
+    if (lay < 2)
+      OperandLayout::row_col(blk, lane, kSteps, row, col);
+    else
+      TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
+    ld_off[i] = int(row * (lay == 1 ? p.v_sn : p.k_sn) * 2) + col * 2;
   }
   const uint16_t* kbase = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
   const uint16_t* vbase = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
-
   auto issue = [&](auto stage, int tile) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
     const int r0 = tile * kTileRows;
     const int rows = min(slen - r0, kTileRows);
     const u32x4 rk = make_rsrc(kbase + int64_t(r0) * p.k_sn, int((rows - 1) * p.k_sn * 2) + D * 2);
     const u32x4 rv = make_rsrc(vbase + int64_t(r0) * p.v_sn, int((rows - 1) * p.v_sn * 2) + D * 2);
-    const uint32_t base = lds0 + ST * kStage + wave * kPer * 1024;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      dma16(rk, base + kKop + i * 1024, op_off_k[i]);
-      dma16(rk, base + kKtr + i * 1024, tr_off_k[i]);
-      dma16(rv, base + kVop + i * 1024, op_off_v[i]);
+    for (int i = 0; i < kPerW; ++i) {
+      const int b = i * kWaves + wave;
+      if (b < kDmaBlocks) {
+        const int lay = b / G::kBlocks, blk = b % G::kBlocks;
+        dma16(lay == 1 ? rv : rk, lds0 + ST * kStage + lay * G::kTileBytes + blk * 1024,
+              ld_off[i]);
+      }
     }
   };
 
@@ -461,74 +481,42 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
     constexpr int ST = decltype(stage)::value;
     const unsigned char* sb = smem + ST * kStage;
     const int r0 = tile * kTileRows;
-    // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves of the tile
-    f32x16 sacc[2], dpacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      dpacc[kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sb + kKop + (kb * kSteps + s) * 1024 +
-                                                        lane * 16);
-        sacc[kb] = E::mfma(a, qf[s], sacc[kb]);
-        const u32x4 g = *reinterpret_cast<const u32x4*>(sb + kVop + (kb * kSteps + s) * 1024 +
-                                                        lane * 16);
-        dpacc[kb] = E::mfma(g, dof[s], dpacc[kb]);
-      }
-    }
-    // entry i of key half kb is key r0 + 32 kb + 8 (i / 4) + 4 half + i % 4
+    const f32x16 sacc = chain_over_d<BF16, kSteps>(sb + kKop + lane * 16, qf);
+    const f32x16 dpacc = chain_over_d<BF16, kSteps>(sb + kVop + lane * 16, dof);
+    // entry i is key r0 + 8 (i / 4) + 4 half + i % 4
     const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 + kTileRows - 1 > qw0);
-    u32x4 pds[2][2];
+    u32x4 pb[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float dsv[16];
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = r0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-        float x = fmaf(sacc[kb][i], p.c, -lse2);
-        if (edge) {
-          const bool ok = key < slen && (!CAUSAL || key <= qrow);
-          x = ok ? x : -INFINITY;
+      for (int w = 0; w < 4; ++w) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 8 * tt + 2 * w + u;
+          float x = fmaf(sacc[i], p.c, nlse);
+          if (edge) {
+            const int kk = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool ok = kk < slen && (!CAUSAL || kk <= qrow);
+            x = ok ? x : -INFINITY;
+          }
+          v2[u] = __builtin_amdgcn_exp2f(x) * (dpacc[i] - del);
         }
-        dsv[i] = __builtin_amdgcn_exp2f(x) * (dpacc[kb][i] - del);
+        pb[tt][w] = E::pack(v2[0], v2[1]);
       }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pds[kb][tt][e] = E::pack(dsv[8 * tt + 2 * e], dsv[8 * tt + 2 * e + 1]);
-    }
-    // dQ^T += K^T dS^T, contracting over the tile's 64 keys
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int j = 0; j < kOBlocks; ++j) {
-          const int blk = ((2 * kb + tt) * kOBlocks + j) * 1024;
-          const u32x2 lo = E::read_tr(sb + kKtr + blk + lane * 8);
-          const u32x2 hi = E::read_tr(sb + kKtr + blk + 512 + lane * 8);
-          dqacc[j] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pds[kb][tt], dqacc[j]);
-        }
-  };
-
-  auto sync = [&]() __attribute__((always_inline)) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __syncthreads();
+    chain_over_rows<BF16, kOBlocks>(sb + kKtr + lane * 8, pb, dqacc);
   };
 
   issue(Int<0>{}, 0);
-  sync();
+  tile_sync();
   for (int t = 0; t < n_tiles; t += 2) {
     if (t + 1 < n_tiles) issue(Int<1>{}, t + 1);
     compute(Int<0>{}, t);
-    sync();
+    tile_sync();
     if (t + 1 < n_tiles) {
       if (t + 2 < n_tiles) issue(Int<0>{}, t + 2);
       compute(Int<1>{}, t + 1);
-      sync();
+      tile_sync();
     }
   }
 
@@ -547,11 +535,11 @@ hipError_t launch_bwd_typed(const BwdArgs& a, int groups, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>),
-                     dim3(a.n_blocks * a.heads_kv * groups), dim3(kBwdThreads), 0, stream, a);
+                     dim3(a.n_kblocks * a.heads_kv * groups), dim3(kThreads8), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, VARLEN>),
-                     dim3(a.n_blocks * a.heads_q * groups), dim3(kBwdThreads), 0, stream, a);
+                     dim3(a.n_qblocks * a.heads_q * groups), dim3(kThreads8), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -594,7 +582,8 @@ fa_status launch_backward(const fa_bwd_params& p, void* stream, const char** hip
   a.group = p.heads_q / p.heads_kv;
   const bool varlen = p.cu_seqlens != nullptr;
   const int rows = varlen ? p.max_seqlen : p.seqlen;
-  a.n_blocks = (rows + kOwn - 1) / kOwn;
+  a.n_kblocks = (rows + 127) / 128;
+  a.n_qblocks = (rows + 255) / 256;
   a.rows_delta = p.batch * p.heads_q * p.seqlen;
   a.c = float((p.scale == 0.f ? 1.0 : std::fabs(double(p.scale))) * 1.4426950408889634);
   a.s_and = p.scale == 0.f ? 0u : 0xFFFFFFFFu;
