@@ -222,9 +222,11 @@ __device__ __forceinline__ void tile_sync() {
 
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
-// each, waves 4-7 dK for the same keys; a SIMD holds one of each. Both roles form S = Q K^T and
-// P; the dK role also dP = dO V^T and dS. Splitting the roles costs S twice (5 products per
-// tile instead of 4) but keeps each wave's state within 256 registers.
+// each, waves 4-7 dK for the same keys; a SIMD holds one of each. Per tile, in two phases
+// separated by a barrier: the dV wave forms S = Q K^T and P (masked), and hands P (fp32) to its
+// dK partner through LDS, while the dK wave forms dP = dO V^T; then the dV wave accumulates
+// dV^T += dO^T P while the dK wave forms dS = P (dP - D) and accumulates dK^T += Q^T dS. Each
+// wave does 16 of the tile's 32 products and keeps its state within 256 registers.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -239,7 +241,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   constexpr int kQop = 0, kDop = G::kTileBytes, kQtr = 2 * G::kTileBytes,
                 kDtr = 3 * G::kTileBytes, kLse = 4 * G::kTileBytes, kDel = kLse + 1024;
   constexpr int kStage = kLse + 2048;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+  constexpr int kPbuf = 2 * kStage;  // P of each key group: 4 x (16 fp32 per lane)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage + 4 * 4096];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -304,72 +307,99 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     }
   };
 
-  // resident K^T (sign of the scale applied) for both roles, V^T for the dK role
-  u32x4 kf[kSteps];
-  load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0, slen,
-                   lane, kf);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) kf[s] = (kf[s] & p.s_and) ^ p.s_xor;
+  // P hand-off: entries 4 g .. 4 g + 3 of lane L at 1 KB block g, byte 16 L
+  unsigned char* pbuf = smem + kPbuf + (wave & 3) * 4096 + lane * 16;
 
   // one role's loop; both roles run the same barriers
   auto run = [&](auto role_c) __attribute__((always_inline)) {
     constexpr bool DK = decltype(role_c)::value;
-    u32x4 vf[kSteps];
-    if constexpr (DK)
+    // resident B operand: K^T (sign of the scale applied) for the dV role, V^T for the dK role
+    u32x4 rf[kSteps];
+    if constexpr (DK) {
       load_resident<D>(p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn, p.v_sn, kw0,
-                       slen, lane, vf);
+                       slen, lane, rf);
+    } else {
+      load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0,
+                       slen, lane, rf);
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) rf[s] = (rf[s] & p.s_and) ^ p.s_xor;
+    }
     f32x16 acc[kOBlocks];
 #pragma unroll
     for (int j = 0; j < kOBlocks; ++j) acc[j] = f32x16{};
+    f32x16 part;   // S (dV role) or dP (dK role) of the current tile
+    u32x4 pb[2];   // P (dV role) packed as the B operand of the row contraction
 
-    auto compute = [&](auto stage, int st) __attribute__((always_inline)) {
+    // phase 1: S and P (dV role, P also stored for the partner) or dP (dK role)
+    auto phase1 = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
-      const int r0 = (t_first + st % per_head) * kTileRows;
-      f32x16 sacc = chain_over_d<BF16, kSteps>(sb + kQop + lane * 16, kf);
-      f32x16 dpacc;
-      if constexpr (DK) dpacc = chain_over_d<BF16, kSteps>(sb + kDop + lane * 16, vf);
-      // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
-      float lse[16], del[16];
-      read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
-      if constexpr (DK) read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
-      const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
-      u32x4 pb[2];
+      part = chain_over_d<BF16, kSteps>(sb + (DK ? kDop : kQop) + lane * 16, rf);
+      if constexpr (!DK) {
+        const int r0 = (t_first + st % per_head) * kTileRows;
+        // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
+        float lse[16], pv[16];
+        read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
+        const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float v2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 8 * tt + 2 * w + u;
-            float x = fmaf(sacc[i], p.c, lse[i] * -kLog2e);
-            if (edge) {
-              const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-              const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
-              x = ok ? x : -INFINITY;
-            }
-            const float pr = __builtin_amdgcn_exp2f(x);
-            v2[u] = DK ? pr * (dpacc[i] - del[i]) : pr;
+        for (int i = 0; i < 16; ++i) {
+          float x = fmaf(part[i], p.c, lse[i] * -kLog2e);
+          if (edge) {
+            const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
+            x = ok ? x : -INFINITY;
           }
-          pb[tt][w] = E::pack(v2[0], v2[1]);
+          pv[i] = __builtin_amdgcn_exp2f(x);
         }
-      // dV^T += dO^T P (dV role) or dK^T += Q^T dS (dK role), over the tile's 32 queries
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(pbuf + g * 1024) =
+              f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
+      }
+    };
+    // phase 2: dV^T += dO^T P (dV role) or dS = P (dP - D), dK^T += Q^T dS (dK role)
+    auto phase2 = [&](auto stage, int st) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage)::value;
+      const unsigned char* sb = smem + ST * kStage;
+      if constexpr (DK) {
+        float del[16];
+        read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
+        float ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(pbuf + g * 1024);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (part[4 * g + r] - del[4 * g + r]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
+      }
       chain_over_rows<BF16, kOBlocks>(sb + (DK ? kQtr : kDtr) + lane * 8, pb, acc);
+    };
+    auto step = [&](auto stage, int st) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage)::value;
+      if (st + 1 < n_steps) issue(Int<1 - ST>{}, st + 1);
+      phase1(Int<ST>{}, st);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P is in LDS
+      __syncthreads();
+      phase2(Int<ST>{}, st);
+      tile_sync();
     };
 
     if (n_steps > 0) {
       issue(Int<0>{}, 0);
       tile_sync();
       for (int st = 0; st < n_steps; st += 2) {
-        if (st + 1 < n_steps) issue(Int<1>{}, st + 1);
-        compute(Int<0>{}, st);
-        tile_sync();
-        if (st + 1 < n_steps) {
-          if (st + 2 < n_steps) issue(Int<0>{}, st + 2);
-          compute(Int<1>{}, st + 1);
-          tile_sync();
-        }
+        step(Int<0>{}, st);
+        if (st + 1 < n_steps) step(Int<1>{}, st + 1);
       }
     }
     if (key < slen) {
