@@ -30,33 +30,41 @@ import seeded_inputs as si  # noqa: E402
 METRIC = "attention fwd TFLOP/s and % of MFMA peak, N=16K d=128 causal bf16"
 # MI355X published dense matrix peaks (TFLOP/s), per input type
 MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0}
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip",
                   "exact_tiled_attention_39_amd/csrc/fa_device.h"]
+SPLITKV_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_splitkv.hip",
+                   "exact_tiled_attention_39_amd/csrc/fa_device.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         h.update((ROOT / rel).read_bytes())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str = "fa_fwd"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source; else None."""
-    path = ROOT / "profiles" / f"fa_fwd_{workload}_traffic.md"
+    path = ROOT / "profiles" / f"{kernel}_{workload}_traffic.md"
     if not path.exists():
         return None
     text = path.read_text()
     src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
+    sources = SPLITKV_SOURCES if kernel == "fa_splitkv" else KERNEL_SOURCES
+    if not src or not val or src.group(1) != kernel_source_hash(sources):
         return None
     return float(val.group(1))
 
 
-def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
-    """The fp64 oracle, as it stands, on seeded query rows until the time budget is spent."""
+def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float, bytes_metric: bool = False
+                 ) -> dict:
+    """The fp64 oracle, as it stands, on seeded query rows until the time budget is spent.
+
+    Reported in TFLOP/s (4*keys*d per row), or with bytes_metric in GB/s: the rows' share of
+    the workload's FLOPs times the workload's minimum bytes, per second."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -64,13 +72,14 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
     rows = si.sample_rows(w, 1 / 64, seed=1234)
     order = np.random.default_rng(99).permutation(len(rows))
     rows = [rows[i] for i in order]
-    cu = inp.cu_seqlens
+    cu, cu_k = inp.cu_seqlens, inp.cu_seqlens_k
     starts = cu[:-1] if cu is not None else None
     done, flops = 0, 0.0
     t0 = time.perf_counter()
     while done < len(rows) and time.perf_counter() - t0 < seconds:
         chunk = rows[done:done + 32]
-        oracle.attention_rows(q, k, v, w.scale, w.causal, chunk, cu_seqlens=cu)
+        oracle.attention_rows(q, k, v, w.scale, w.causal, chunk, cu_seqlens=cu,
+                              cu_seqlens_k=cu_k)
         for _, _, i in chunk:
             if cu is not None:
                 s = int(np.searchsorted(starts, i, side="right")) - 1
@@ -78,8 +87,14 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
                     s += 1
                 s0, s1 = int(cu[s]), int(cu[s + 1])
             else:
-                s0, s1 = 0, w.seqlen
-            nk = w.keys if cu is None else s1 - s0  # keys of the row's sequence
+                s, s0, s1 = 0, 0, w.seqlen
+            # keys of the row's sequence
+            if cu is None:
+                nk = w.keys
+            elif cu_k is not None:
+                nk = int(cu_k[s + 1] - cu_k[s])
+            else:
+                nk = s1 - s0
             shift = nk - (s1 - s0)  # the queries are the last positions of the keys
             keys = min(nk, i - s0 + shift + 1) if w.causal else nk
             flops += 4.0 * max(keys, 0) * w.head_dim
@@ -88,14 +103,20 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float) -> dict:
     threads = max([p.get("num_threads", 1) for p in threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
     total_rows = w.batch * w.heads_q * w.seqlen
+    if bytes_metric:
+        value, unit = flops / w.flops() * w.io_bytes() / elapsed / 1e9, "GB/s"
+    else:
+        value, unit = flops / elapsed / 1e12, "TFLOP/s"
     return {
-        "value": flops / elapsed / 1e12,
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"{done} seeded query rows of {total_rows} ({done / total_rows:.2e} of the "
-                   f"workload), {elapsed:.1f} s, fp64, same FLOP convention per row "
-                   f"(4*keys*d)"),
+                   f"workload), {elapsed:.1f} s, fp64, "
+                   + ("rows weighted by their share of the workload's FLOPs (4*keys*d), "
+                      "times its minimum bytes" if bytes_metric else
+                      "same FLOP convention per row (4*keys*d)")),
     }
 
 
@@ -203,6 +224,99 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
     return 0
 
 
+def bench_splitkv(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> int:
+    """The split-KV forward (split and merge kernels) of a decode workload, in GB/s of the
+    bytes it must move."""
+    import oracle
+
+    dev = q.device
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
+    cu_k = torch.from_numpy(inp.cu_seqlens_k).to(dev) if inp.cu_seqlens_k is not None else None
+    max_seqlen = w.max_seqlen() if w.varlen else None
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    params = fa.make_params(q, k, v, o, lse, w.scale, w.causal, cu, max_seqlen, cu_k)
+    splits, ws_bytes = fa.fa_splitkv_plan(params, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
+    def step():
+        fa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale=w.scale, causal=w.causal, num_splits=0,
+                          cu_seqlens=cu, max_seqlen=max_seqlen, cu_seqlens_k=cu_k)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [a.elapsed_time(b) for a, b in events]
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    nbytes = w.io_bytes()
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    avg_ms = float(np.mean(launch_ms))
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+
+    rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
+    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
+                                           cu_seqlens=inp.cu_seqlens,
+                                           cu_seqlens_k=inp.cu_seqlens_k)
+    del qf, kf, vf
+    idx = tuple(np.array(rows).T)
+    o_gpu = si.bits_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16)[idx], w.dtype)
+    lse_gpu = lse.cpu().numpy().astype(np.float64)[idx]
+    line = {
+        "metric": f"attention decode GB/s (Q, K, V read, O, LSE written), {w.name}",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, see seeded_inputs.py)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+            "seqlen": w.seqlen, "seqlen_k": w.keys, "head_dim": w.head_dim, "causal": w.causal,
+            "num_seqs": len(w.seq_lens) if w.varlen else None, "splits": splits,
+            "workspace_bytes": ws_bytes, "io_bytes": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.name, "fa_splitkv"),
+            "kernel": "fa_fwd_splitkv (fa_splitkv_kernel + fa_splitkv_merge_kernel)",
+            "avg_launch_ms": round(avg_ms, 4),
+            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        },
+        "parity": {
+            "rows": len(rows),
+            "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
+            "max_lse_err": float((np.abs(lse_gpu - lse_ref)
+                                  / np.maximum(np.abs(lse_ref), 1)).max()),
+        },
+        "kernel_source_sha256": kernel_source_hash(SPLITKV_SOURCES),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, bytes_metric=True)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +359,8 @@ def main() -> int:
     q, k, v = up(inp.q), up(inp.k), up(inp.v)
     if args.backward:
         return bench_backward(args, torch, fa, w, inp, q, k, v, up)
+    if w.splitkv:
+        return bench_splitkv(args, torch, fa, w, inp, q, k, v)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None

@@ -6,10 +6,11 @@ raises ``FaError`` on any non-OK status. There is no fallback: if the library is
 import of the binding functions raises.
 
 The C entry points (include/fa.h) are mirrored with the same names:
-``fa_fwd``, ``fa_check_args``, ``fa_bwd``, ``fa_bwd_check_args``, ``fa_status_string``,
-``fa_abi_version``, ``fa_params_size``, ``fa_bwd_params_size``. ``attention`` allocates O and
-LSE and calls ``fa_fwd``; ``attention_backward`` allocates dQ, dK, dV and the delta workspace
-and calls ``fa_bwd``.
+``fa_fwd``, ``fa_check_args``, ``fa_splitkv_plan``, ``fa_fwd_splitkv``, ``fa_bwd``,
+``fa_bwd_check_args``, ``fa_status_string``, ``fa_abi_version``, ``fa_params_size``,
+``fa_bwd_params_size``. ``attention`` allocates O and LSE and calls ``fa_fwd``;
+``attention_splitkv`` allocates O, LSE and the split workspace and calls ``fa_fwd_splitkv``;
+``attention_backward`` allocates dQ, dK, dV and the delta workspace and calls ``fa_bwd``.
 """
 from __future__ import annotations
 
@@ -25,7 +26,8 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 FA_F16, FA_BF16 = 0, 1
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 3
+FA_ABI_VERSION = 4
+FA_MAX_SPLITS = 256
 
 _I64x3 = ctypes.c_int64 * 3
 
@@ -134,6 +136,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [ctypes.c_int32]
+    lib.fa_splitkv_plan.restype = ctypes.c_int32
+    lib.fa_splitkv_plan.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_uint64)]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int32
+    lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_uint64, ctypes.c_void_p]
     lib.fa_bwd_params_size.restype = ctypes.c_uint32
     lib.fa_bwd_params_size.argtypes = []
     lib.fa_bwd_check_args.restype = ctypes.c_int32
@@ -275,6 +284,66 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
            max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k)
+    return o, lse
+
+
+def fa_splitkv_plan(params: FaFwdParams, num_splits: int = 0) -> Tuple[int, int]:
+    """Host-only: (resolved split count, workspace bytes) for fa_fwd_splitkv; raises FaError."""
+    splits = ctypes.c_int32(0)
+    nbytes = ctypes.c_uint64(0)
+    st = int(load_library().fa_splitkv_plan(ctypes.byref(params), int(num_splits),
+                                            ctypes.byref(splits), ctypes.byref(nbytes)))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return int(splits.value), int(nbytes.value)
+
+
+def fa_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, workspace: Optional[torch.Tensor], *, scale: float,
+                   causal: bool = False, num_splits: int = 0,
+                   cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                   stream: Optional[torch.cuda.Stream] = None,
+                   cu_seqlens_k: Optional[torch.Tensor] = None) -> None:
+    """Enqueues the split-KV forward writing o and lse; `workspace` is a device tensor of at
+    least fa_splitkv_plan's byte count (None when that is 0)."""
+    lib = load_library()
+    for t in (q, k, v, o, lse) + ((workspace,) if workspace is not None else ()):
+        if not t.is_cuda:
+            raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = int(lib.fa_fwd_splitkv(ctypes.byref(p), int(num_splits), ctypes.c_void_p(ws_ptr),
+                                    ctypes.c_uint64(ws_bytes), ctypes.c_void_p(s.cuda_stream)))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+
+
+def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                      scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      max_seqlen: Optional[int] = None,
+                      cu_seqlens_k: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``attention`` computed by the split-KV kernels (meant for a few queries per sequence
+    against many keys); allocates O, LSE and the workspace."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if cu_seqlens is not None and max_seqlen is None:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+        max_seqlen = int(lens.max()) if lens.numel() else 0
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
+    _, nbytes = fa_splitkv_plan(p, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    fa_fwd_splitkv(q, k, v, o, lse, ws, scale=scale, causal=causal, num_splits=num_splits,
+                   cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k)
     return o, lse
 
 

@@ -89,6 +89,48 @@ fa_status fa_fwd(const fa_fwd_params* p, void* stream) {
   return ls;
 }
 
+namespace {
+
+// The split-KV plan for validated arguments, or FA_ERR_SHAPE when a grid would not fit.
+fa_status checked_plan(const fa_fwd_params* p, int32_t num_splits, fa::SplitPlan* plan) {
+  const fa_status st = fa_check_args(p);
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
+  *plan = fa::plan_splitkv(*p, num_splits);
+  if (plan->grid > INT32_MAX || (plan->rows_total + 3) / 4 > INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_splitkv_plan(const fa_fwd_params* p, int32_t num_splits, int32_t* splits,
+                          uint64_t* workspace_bytes) {
+  fa::SplitPlan plan;
+  const fa_status st = checked_plan(p, num_splits, &plan);
+  if (st != FA_OK) return st;
+  if (splits != nullptr) *splits = plan.splits;
+  if (workspace_bytes != nullptr) *workspace_bytes = plan.workspace_bytes;
+  return FA_OK;
+}
+
+fa_status fa_fwd_splitkv(const fa_fwd_params* p, int32_t num_splits, void* workspace,
+                         uint64_t workspace_bytes, void* stream) {
+  fa::SplitPlan plan;
+  const fa_status st = checked_plan(p, num_splits, &plan);
+  if (st != FA_OK) return st;
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr) return FA_ERR_NULL;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if (workspace_bytes < plan.workspace_bytes) return FA_ERR_SHAPE;
+  }
+  if (p->seqlen == 0) return FA_OK;
+  if (p->cu_seqlens != nullptr && p->max_seqlen == 0) return FA_OK;
+  const char* err = nullptr;
+  const fa_status ls = fa::launch_forward_splitkv(*p, plan, workspace, stream, &err);
+  if (ls != FA_OK && err != nullptr) g_last_hip_error = err;
+  return ls;
+}
+
 uint32_t fa_bwd_params_size(void) { return static_cast<uint32_t>(sizeof(fa_bwd_params)); }
 
 fa_status fa_bwd_check_args(const fa_bwd_params* p) {

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -187,6 +187,44 @@ fa_status fa_check_args(const fa_fwd_params* p);
  * caller's next synchronisation of the stream. NaN or Inf inputs are not checked and propagate.
  */
 fa_status fa_fwd(const fa_fwd_params* p, void* stream);
+
+/*
+ * Split-KV forward: the outputs of fa_fwd (O and LSE, to rounding) for the same arguments,
+ * organised for query chunks of a few tokens against a long key/value context (token-by-token
+ * decode with a KV cache, the composition the "Flash Attention" notes name in "Connection to
+ * the Broader Curriculum"). The query rows of every head that shares a kv head are packed into
+ * one block, so each key/value tile is read once per head group, and the keys of every
+ * (sequence, kv head) are divided into num_splits contiguous ranges that run as separate
+ * workgroups. Each range keeps its own online-softmax state (Theorem 2 of the notes) and writes
+ * a partial output normalised by its own sum, with its log-sum-exp, to `workspace`; a second
+ * kernel merges the partials with the same rescaling rule. With one split the first kernel
+ * writes O and LSE itself and no workspace is used. Any seqlen works, but for long query
+ * chunks fa_fwd is the faster call.
+ *
+ * num_splits: 1 .. FA_MAX_SPLITS, or 0 for the library's choice from the shapes (the same
+ * choice in both calls below). The choice is a function of the arguments only.
+ */
+#define FA_MAX_SPLITS 256
+
+/*
+ * Host only: resolves num_splits (into *splits, if not NULL) and the workspace bytes
+ * fa_fwd_splitkv needs with it (into *workspace_bytes, if not NULL; 0 for one split).
+ * Errors: those of fa_check_args; FA_ERR_SHAPE for num_splits outside [0, FA_MAX_SPLITS] or a
+ * grid that would not fit.
+ */
+fa_status fa_splitkv_plan(const fa_fwd_params* p, int32_t num_splits, int32_t* splits,
+                          uint64_t* workspace_bytes);
+
+/*
+ * Enqueue the split-KV forward on `stream`. workspace: caller-owned device memory, 16-byte
+ * aligned, of at least the planned bytes (workspace_bytes gives its size); it may be NULL when
+ * the plan needs none. Its contents on entry do not matter and on return are unspecified;
+ * calls that may run at the same time need their own workspace. Errors: those of
+ * fa_splitkv_plan; FA_ERR_NULL for a missing workspace, FA_ERR_ALIGN for a misaligned one,
+ * FA_ERR_SHAPE for one that is too small; all before any device call.
+ */
+fa_status fa_fwd_splitkv(const fa_fwd_params* p, int32_t num_splits, void* workspace,
+                         uint64_t workspace_bytes, void* stream);
 
 /* sizeof(fa_bwd_params) as compiled into the library. */
 uint32_t fa_bwd_params_size(void);

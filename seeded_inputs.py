@@ -10,7 +10,10 @@ batch x heads x N x d, a scale, a causal flag, a GQA head ratio, packed variable
 sequences). The shape of the second one is the SDPA usage example on the FromZero2AI page
 ("FlashAttention: GPU Memory-Bound Speedups for Long-Context LLMs", section "Code Verification").
 The sixth is a query chunk against a longer key/value context (chunked prefill with a KV
-cache, xspy page "FlashAttention and chunked prefill mechanics", section 1).
+cache, xspy page "FlashAttention and chunked prefill mechanics", section 1). The last two are
+decode steps against a KV cache (one new query token per sequence; the cache the notes list
+among the compositions of the method, "Connection to the Broader Curriculum"): a batch of equal
+cache lengths, and packed sequences whose cache lengths are drawn uniformly from a range.
 
 Draw order per workload: (varlen only) the sequence lengths, then Q, then K, then V, each as
 float32 standard normals in C order of shape [B, H, N, d] (K and V with the key length); the
@@ -44,6 +47,8 @@ class Workload:
     qk_multiplier: float = 1.0
     seq_lens: Optional[Tuple[int, ...]] = None  # varlen only (batch == 1)
     seqlen_k: Optional[int] = None  # keys per batch entry when it differs from seqlen
+    seq_lens_k: Optional[Tuple[int, ...]] = None  # varlen keys, when packed unlike the queries
+    splitkv: bool = False  # run by the split-KV entry point (few queries per sequence)
 
     @property
     def scale(self) -> float:
@@ -58,11 +63,17 @@ class Workload:
             return None
         return np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int32)
 
+    def cu_seqlens_k(self) -> Optional[np.ndarray]:
+        if self.seq_lens_k is None:
+            return None
+        return np.concatenate([[0], np.cumsum(self.seq_lens_k)]).astype(np.int32)
+
     def max_seqlen(self) -> int:
         return max(self.seq_lens) if self.seq_lens is not None else self.seqlen
 
     @property
     def keys(self) -> int:
+        """Key tokens per batch entry (packed total for varlen)."""
         return self.seqlen if self.seqlen_k is None else self.seqlen_k
 
     def flops(self) -> float:
@@ -71,6 +82,10 @@ class Workload:
         For packed sequences the count is summed per sequence. With Nq queries against Nk keys
         it is 4*Nq*Nk*d, less 2*Nq^2*d when causal (the same convention at Nq == Nk).
         """
+        if self.seq_lens_k is not None:
+            per = sum(4.0 * self.head_dim * (nq * nk - (nq * nq / 2.0 if self.causal else 0.0))
+                      for nq, nk in zip(self.seq_lens, self.seq_lens_k))
+            return per * self.heads_q
         if self.seqlen_k is not None:
             nq, nk = self.seqlen, self.seqlen_k
             per = 4.0 * self.head_dim * (nq * nk - (nq * nq / 2.0 if self.causal else 0.0))
@@ -78,6 +93,14 @@ class Workload:
         lens = self.seq_lens if self.seq_lens is not None else (self.seqlen,) * self.batch
         per = sum(4.0 * n * n * self.head_dim for n in lens) * self.heads_q
         return per / 2.0 if self.causal else per
+
+
+    def io_bytes(self) -> int:
+        """Bytes one forward call must move at least: Q, K, V read once, O written (all in the
+        2-byte input type), fp32 LSE written."""
+        q_elems = self.batch * self.heads_q * self.seqlen * self.head_dim
+        kv_elems = self.batch * self.heads_kv * self.keys * self.head_dim
+        return 2 * (2 * q_elems + 2 * kv_elems) + 4 * self.batch * self.heads_q * self.seqlen
 
 
 def _varlen_lengths(seed: int, count: int, lo: int, hi: int) -> Tuple[int, ...]:
@@ -91,6 +114,12 @@ def _c5() -> Workload:
                     seq_lens=lens)
 
 
+def _decode_varlen() -> Workload:
+    lens_k = _varlen_lengths(8, 32, 256, 16384)
+    return Workload("decode_varlen32_hq32_hkv8_d128_bf16", 1, 32, 8, 32, 128, BF16, True, 8,
+                    seq_lens=(1,) * 32, seqlen_k=sum(lens_k), seq_lens_k=lens_k, splitkv=True)
+
+
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -102,6 +131,9 @@ WORKLOADS: Dict[str, Workload] = {
         _c5(),
         Workload("chunk_b1_hq32_hkv8_q2048_k16384_d128_causal_bf16", 1, 32, 8, 2048, 128, BF16,
                  True, 6, seqlen_k=16384),
+        Workload("decode_b16_hq32_hkv8_q1_k16384_d128_bf16", 16, 32, 8, 1, 128, BF16, True, 7,
+                 seqlen_k=16384, splitkv=True),
+        _decode_varlen(),
     ]
 }
 WORKLOAD_ORDER: List[str] = list(WORKLOADS)
@@ -118,10 +150,14 @@ def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == F16:
         return x.astype(np.float16).view(np.uint16)
     if dtype == BF16:
-        u = x.view(np.uint32).astype(np.uint64)
-        rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        # u + 0x7FFF + lsb only wraps past 2^32 for NaN patterns, which are replaced below
+        u = x.view(np.uint32)
+        r = (u >> 16) & np.uint32(1)
+        r += u
+        r += np.uint32(0x7FFF)
+        r >>= 16
+        out = r.astype(np.uint16)
         nan = np.isnan(x)
-        out = rounded.astype(np.uint16)
         if nan.any():
             out[nan] = 0x7FC0
         return out
@@ -221,7 +257,7 @@ def workload_inputs(w: Workload) -> Inputs:
     """The seeded inputs of a named workload (the varlen lengths are part of the workload)."""
     return random_inputs(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, w.dtype, w.seed,
                          causal=w.causal, scale=w.scale, qk_multiplier=w.qk_multiplier,
-                         seq_lens=w.seq_lens, seqlen_k=w.seqlen_k)
+                         seq_lens=w.seq_lens, seqlen_k=w.seqlen_k, seq_lens_k=w.seq_lens_k)
 
 
 # ----------------------------------------------------------------------------------------

@@ -23,7 +23,9 @@ def download_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(inp: si.Inputs, device="cuda", max_seqlen=None):
+def run(inp: si.Inputs, device="cuda", max_seqlen=None, splits=None):
+    """O (float64 of the output bits) and LSE of fa_fwd, or of fa_fwd_splitkv with `splits`
+    (0: the library's choice)."""
     import exact_tiled_attention_39_amd as fa
 
     q = upload(inp.q, inp.dtype, device)
@@ -36,8 +38,13 @@ def run(inp: si.Inputs, device="cuda", max_seqlen=None):
             max_seqlen = int(np.diff(inp.cu_seqlens).max()) if len(inp.cu_seqlens) > 1 else 0
     if inp.cu_seqlens_k is not None:
         cu_k = torch.from_numpy(inp.cu_seqlens_k).to(device)
-    o, lse = fa.attention(q, k, v, scale=inp.scale, causal=inp.causal, cu_seqlens=cu,
-                          max_seqlen=max_seqlen, cu_seqlens_k=cu_k)
+    if splits is None:
+        o, lse = fa.attention(q, k, v, scale=inp.scale, causal=inp.causal, cu_seqlens=cu,
+                              max_seqlen=max_seqlen, cu_seqlens_k=cu_k)
+    else:
+        o, lse = fa.attention_splitkv(q, k, v, scale=inp.scale, causal=inp.causal,
+                                      num_splits=splits, cu_seqlens=cu, max_seqlen=max_seqlen,
+                                      cu_seqlens_k=cu_k)
     torch.cuda.synchronize()
     return si.bits_to_f64(download_bits(o), inp.dtype), lse.cpu().numpy().astype(np.float64)
 

@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_check_args",
                                     "fa_bwd_params_size", "fa_check_args", "fa_fwd",
-                                    "fa_params_size", "fa_status_string"]
+                                    "fa_fwd_splitkv", "fa_params_size", "fa_splitkv_plan",
+                                    "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -126,6 +127,58 @@ def test_empty_problem_is_a_no_op():
     p = good(seqlen=0, q=0, k=0, v=0, o=0, lse=0)
     lib = fa.load_library()
     assert lib.fa_fwd(ctypes.byref(p), None) == fa.FA_OK
+
+
+def decode_params(**kw):
+    """16 sequences, one query each, 32 query heads on 8 kv heads, 16384 cached keys."""
+    base = dict(batch=16, heads_q=32, heads_kv=8, seqlen=1, seqlen_k=16384, causal=1,
+                q_stride=(32 * 128, 128, 128), o_stride=(32 * 128, 128, 128),
+                k_stride=(8 * 16384 * 128, 16384 * 128, 128),
+                v_stride=(8 * 16384 * 128, 16384 * 128, 128))
+    base.update(kw)
+    return good(**base)
+
+
+def test_splitkv_plan():
+    rows_total = 16 * 32 * 1
+    # 128 (sequence, kv head) items, one 32-row block each: 1536 / 128 = 12 splits
+    assert fa.fa_splitkv_plan(decode_params(), 0) == (12, 12 * rows_total * 129 * 4)
+    assert fa.fa_splitkv_plan(decode_params(), 1) == (1, 0)
+    assert fa.fa_splitkv_plan(decode_params(), 5) == (5, 5 * rows_total * 129 * 4)
+    assert fa.fa_splitkv_plan(decode_params(head_dim=64), 3) == (3, 3 * rows_total * 65 * 4)
+    # few keys: at least four 32-key tiles per split
+    assert fa.fa_splitkv_plan(decode_params(seqlen_k=300), 0)[0] == 2
+    assert fa.fa_splitkv_plan(decode_params(seqlen_k=0, k=0, v=0), 0)[0] == 1
+    # many items: one split
+    assert fa.fa_splitkv_plan(decode_params(batch=256), 0)[0] == 1
+    assert fa.fa_splitkv_plan(decode_params(), fa.FA_MAX_SPLITS)[0] == fa.FA_MAX_SPLITS
+
+
+@pytest.mark.parametrize("splits", [-1, 257])
+def test_splitkv_rejects_split_counts(splits):
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_splitkv_plan(decode_params(), splits)
+    assert e.value.status == fa.FA_ERR_SHAPE
+    lib = fa.load_library()
+    assert lib.fa_fwd_splitkv(ctypes.byref(decode_params()), splits, ALIGNED * 8, 2 ** 30,
+                              None) == fa.FA_ERR_SHAPE
+
+
+def test_splitkv_workspace_errors_before_any_device_call():
+    lib = fa.load_library()
+    p = decode_params()
+    _, need = fa.fa_splitkv_plan(p, 4)
+    assert lib.fa_fwd_splitkv(ctypes.byref(p), 4, None, need, None) == fa.FA_ERR_NULL
+    assert lib.fa_fwd_splitkv(ctypes.byref(p), 4, ALIGNED * 8 + 4, need, None) == fa.FA_ERR_ALIGN
+    assert lib.fa_fwd_splitkv(ctypes.byref(p), 4, ALIGNED * 8, need - 1, None) == fa.FA_ERR_SHAPE
+    # argument errors of fa_fwd come first
+    assert lib.fa_fwd_splitkv(ctypes.byref(decode_params(heads_kv=3)), 4, ALIGNED * 8, need,
+                              None) == fa.FA_ERR_GQA
+    assert lib.fa_fwd_splitkv(None, 0, None, 0, None) == fa.FA_ERR_NULL
+    # no rows: a no-op that needs no workspace
+    empty = decode_params(seqlen=0, q=0, o=0, lse=0)
+    assert fa.fa_splitkv_plan(empty, 4) == (4, 0)
+    assert lib.fa_fwd_splitkv(ctypes.byref(empty), 4, None, 0, None) == fa.FA_OK
 
 
 def test_status_strings():

@@ -263,18 +263,27 @@ def test_workload_full_size(name):
     inp = si.workload_inputs(w)
     q, k, v = (upload(x, w.dtype) for x in (inp.q, inp.k, inp.v))
     cu = torch.from_numpy(inp.cu_seqlens).cuda() if w.varlen else None
-    o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, cu_seqlens=cu,
-                          max_seqlen=w.max_seqlen() if w.varlen else None)
-    assert w.seqlen_k is None or k.shape[2] == w.seqlen_k
+    cu_k = torch.from_numpy(inp.cu_seqlens_k).cuda() if inp.cu_seqlens_k is not None else None
+    kw = dict(scale=w.scale, causal=w.causal, cu_seqlens=cu,
+              max_seqlen=w.max_seqlen() if w.varlen else None, cu_seqlens_k=cu_k)
+    # decode workloads run through both entry points
+    runs = [("fa_fwd", fa.attention(q, k, v, **kw))]
+    if w.splitkv:
+        runs.append(("fa_fwd_splitkv", fa.attention_splitkv(q, k, v, **kw)))
+    assert k.shape[2] == w.keys
     torch.cuda.synchronize()
-    o_bits = download_bits(o)
-    lse = lse.cpu().numpy().astype(np.float64)
-    del q, k, v, o
+    results = [(entry, download_bits(o), l.cpu().numpy().astype(np.float64))
+               for entry, (o, l) in runs]
+    del q, k, v, runs
     qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
     if w.batch * w.heads_q * w.seqlen <= 2 ** 17:
-        o_ref, lse_ref = oracle.attention(qf, kf, vf, w.scale, w.causal, cu_seqlens=inp.cu_seqlens)
-        assert_close(si.bits_to_f64(o_bits, w.dtype), lse, o_ref, lse_ref, w.dtype, name)
+        o_ref, lse_ref = oracle.attention(qf, kf, vf, w.scale, w.causal, cu_seqlens=inp.cu_seqlens,
+                                          cu_seqlens_k=inp.cu_seqlens_k)
+        for entry, o_bits, lse in results:
+            assert_close(si.bits_to_f64(o_bits, w.dtype), lse, o_ref, lse_ref, w.dtype,
+                         f"{name} via {entry}")
     else:
+        (_, o_bits, lse), = results
         rows = si.sample_rows(w, 1 / 512, seed=w.seed)
         o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
                                                cu_seqlens=inp.cu_seqlens)

@@ -46,7 +46,7 @@ def test_same_seed_same_bits():
 
 def test_named_workloads():
     w = si.WORKLOADS
-    assert list(w) == si.WORKLOAD_ORDER and len(w) == 6
+    assert list(w) == si.WORKLOAD_ORDER and len(w) == 8
     c5 = w["varlen16_h16_d128_causal_bf16"]
     assert c5.seq_lens == (5664, 6695, 685, 6717, 4113, 4470, 5352, 2707, 8035, 926, 2646,
                            3456, 4899, 3649, 1518, 859)
@@ -61,6 +61,16 @@ def test_named_workloads():
     # causal chunk: query i of 2048 sees 16384 - 2048 + i + 1 keys; 4*d per key, 32 heads
     exact = 4 * 128 * 32 * sum(16384 - 2048 + i + 1 for i in range(2048))
     assert abs(ch.flops() - exact) / exact < 1e-3
+    dec = w["decode_b16_hq32_hkv8_q1_k16384_d128_bf16"]
+    assert dec.splitkv and (dec.batch, dec.seqlen, dec.keys) == (16, 1, 16384)
+    # K and V of 16 x 8 heads x 16384 keys x 128 dims, 2 bytes each, dominate the bytes moved
+    assert dec.io_bytes() == 2 * (2 * 16 * 32 * 128 + 2 * 16 * 8 * 16384 * 128) + 4 * 16 * 32
+    dv = w["decode_varlen32_hq32_hkv8_d128_bf16"]
+    assert dv.seq_lens == (1,) * 32 and len(dv.seq_lens_k) == 32
+    assert all(256 <= n <= 16384 for n in dv.seq_lens_k)
+    assert dv.keys == sum(dv.seq_lens_k) == dv.cu_seqlens_k()[-1]
+    # one causal query at the end of each cache sees every key: 4 d flops per key and head
+    assert math.isclose(dv.flops(), sum(4.0 * 128 * (nk - 0.5) for nk in dv.seq_lens_k) * 32)
 
 
 def test_key_length_inputs():
