@@ -69,7 +69,12 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float, bytes_metric: b
     from threadpoolctl import threadpool_info
 
     q, k, v = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
-    rows = si.sample_rows(w, 1 / 64, seed=1234)
+    total_rows = w.batch * w.heads_q * w.seqlen
+    if total_rows <= 4096:  # few query rows (decode): every row, in seeded order
+        rows = [(b, h, t) for b in range(w.batch) for h in range(w.heads_q)
+                for t in range(w.seqlen)]
+    else:
+        rows = si.sample_rows(w, 1 / 64, seed=1234)
     order = np.random.default_rng(99).permutation(len(rows))
     rows = [rows[i] for i in order]
     cu, cu_k = inp.cu_seqlens, inp.cu_seqlens_k
@@ -102,7 +107,6 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float, bytes_metric: b
     elapsed = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
-    total_rows = w.batch * w.heads_q * w.seqlen
     if bytes_metric:
         value, unit = flops / w.flops() * w.io_bytes() / elapsed / 1e9, "GB/s"
     else:

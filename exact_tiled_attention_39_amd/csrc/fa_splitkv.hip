@@ -321,22 +321,33 @@ void fa_splitkv_merge_kernel(const SplitArgs p) {
   const int b = int(bh / p.heads_q);
   const int h = int(bh - int64_t(b) * p.heads_q);
 
+  // The row's maximum L_z: lane l reads splits l, l + 64, ...
   float m = -INFINITY;
-  for (int z = 0; z < p.splits; ++z) m = fmaxf(m, p.ws_lse[int64_t(z) * p.rows_total + ridx]);
+  for (int z = lane; z < p.splits; z += 64)
+    m = fmaxf(m, p.ws_lse[int64_t(z) * p.rows_total + ridx]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int z = 0; z < p.splits; ++z) {
-      const int64_t widx = int64_t(z) * p.rows_total + ridx;
-      const float lz = p.ws_lse[widx];
-      if (lz == -INFINITY) continue;  // its O_z was never written
-      const float w = __builtin_amdgcn_exp2f(lz - m);
-      wsum += w;
-      const float* src = p.ws_o + widx * D + lane * kPer;
+    for (int z0 = 0; z0 < p.splits; z0 += 64) {
+      // lane l holds the weight of split z0 + l (0 for a split that saw no key: its O_z was
+      // never written, so it is selected away rather than multiplied)
+      const int zl = z0 + lane;
+      const float lz = zl < p.splits ? p.ws_lse[int64_t(zl) * p.rows_total + ridx] : -INFINITY;
+      const float wl = lz == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lz - m);
+      const int cnt = min(64, p.splits - z0);
+      // independent loads, issued back to back
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) {
+        const float w = __shfl(wl, j);
+        const float* src = p.ws_o + (int64_t(z0 + j) * p.rows_total + ridx) * D + lane * kPer;
+        wsum += w;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+        for (int e = 0; e < kPer; ++e) acc[e] += w != 0.f ? w * src[e] : 0.f;
+      }
     }
   }
   const bool none = m == -INFINITY;
@@ -384,13 +395,18 @@ SplitPlan plan_splitkv(const fa_fwd_params& p, int32_t num_splits) {
   plan.rowblocks = (group * rows + kBlockRows - 1) / kBlockRows;
   int64_t splits = num_splits;
   if (splits == 0) {
-    // Enough workgroups for every CU to hold three (their LDS limit) about twice over, and
-    // at least four tiles (128 keys) per split. Packed sequences are sized by their mean.
-    const int64_t keys = varlen ? (p.seqlen_k + groups - 1) / groups : p.seqlen_k;
-    const int64_t tiles = (keys + kTileKeys - 1) / kTileKeys;
+    // The LDS of all CUs holds three workgroups of the split kernel per CU, 768 at once. Each
+    // workgroup pays a pipeline fill (its first tiles' full memory latency), so with equal
+    // keys per sequence one round of equal workgroups is best (measured: 1 round 189 us, 2
+    // rounds 201 us, 4 rounds 221 us for 16 sequences x 8 kv heads x 16K keys). Packed
+    // sequences of unequal lengths take two rounds, which lets the short splits fill in
+    // around the long ones. At least four tiles (128 keys) per split.
+    constexpr int64_t kResident = 256 * 3;
+    const int64_t rounds = varlen ? 2 : 1;
     const int64_t units = std::max<int64_t>(groups * p.heads_kv * plan.rowblocks, 1);
-    constexpr int64_t kTargetGroups = 256 * 3 * 2;
-    splits = (kTargetGroups + units - 1) / units;
+    const int64_t keys = varlen ? (int64_t(p.seqlen_k) + groups - 1) / groups : p.seqlen_k;
+    const int64_t tiles = (keys + kTileKeys - 1) / kTileKeys;
+    splits = (kResident * rounds + units - 1) / units;
     splits = std::min(splits, std::max<int64_t>(tiles / 4, 1));
     splits = std::min<int64_t>(std::max<int64_t>(splits, 1), FA_MAX_SPLITS);
   }

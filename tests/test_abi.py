@@ -141,8 +141,9 @@ def decode_params(**kw):
 
 def test_splitkv_plan():
     rows_total = 16 * 32 * 1
-    # 128 (sequence, kv head) items, one 32-row block each: 1536 / 128 = 12 splits
-    assert fa.fa_splitkv_plan(decode_params(), 0) == (12, 12 * rows_total * 129 * 4)
+    # 128 (sequence, kv head) items, one 32-row block each: 3 workgroups per CU on 256 CUs
+    # make one round of 768, so 768 / 128 = 6 splits
+    assert fa.fa_splitkv_plan(decode_params(), 0) == (6, 6 * rows_total * 129 * 4)
     assert fa.fa_splitkv_plan(decode_params(), 1) == (1, 0)
     assert fa.fa_splitkv_plan(decode_params(), 5) == (5, 5 * rows_total * 129 * 4)
     assert fa.fa_splitkv_plan(decode_params(head_dim=64), 3) == (3, 3 * rows_total * 65 * 4)
@@ -152,6 +153,19 @@ def test_splitkv_plan():
     # many items: one split
     assert fa.fa_splitkv_plan(decode_params(batch=256), 0)[0] == 1
     assert fa.fa_splitkv_plan(decode_params(), fa.FA_MAX_SPLITS)[0] == fa.FA_MAX_SPLITS
+
+
+def test_splitkv_plan_for_packed_cache_lengths():
+    """32 packed sequences, 254094 keys in all: two rounds of 768 workgroups over 32 x 8
+    (sequence, kv head) items is 6 splits each."""
+    p = decode_params(batch=1, seqlen=32, seqlen_k=254094, cu_seqlens=ALIGNED * 6,
+                      cu_seqlens_k=ALIGNED * 7, num_seqs=32, max_seqlen=1,
+                      q_stride=(32 * 32 * 128, 32 * 128, 128), o_stride=(32 * 32 * 128, 32 * 128, 128),
+                      k_stride=(8 * 254094 * 128, 254094 * 128, 128),
+                      v_stride=(8 * 254094 * 128, 254094 * 128, 128))
+    splits, nbytes = fa.fa_splitkv_plan(p, 0)
+    assert splits == 6 and nbytes == 6 * 32 * 32 * 129 * 4
+    assert fa.fa_splitkv_plan(p, 5)[0] == 5
 
 
 @pytest.mark.parametrize("splits", [-1, 257])
