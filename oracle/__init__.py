@@ -18,6 +18,9 @@ What it computes, with the passages it follows:
   pin the definition against the pages' claim that tiling is exact.
 * ``scalar``: pure-Python (math.fsum) brute force and the two-pass online normaliser of the xspy
   page's section 3, for tiny inputs.
+* ``rope``: rotary position embedding in front of the definition (the RoPE of the notes'
+  "Flash Attention 2 Improvements" list): the standard tables, the exact rotation, the rounded
+  fp32 rotation of the reading, per-sequence positions, and ``attention_rope``.
 * ``attention_backward``: the exact gradients dQ, dK, dV of the definition (the chain rule through
   the materialised softmax), which the recomputing backward pass of the notes' Pitfall 3 and
   the FromZero2AI page's mechanism 3 must reproduce.
@@ -30,7 +33,7 @@ from .definition import (attention, attention_rows, kv_head, score_matrix_bytes,
 from .online import flash_forward, merge
 from .backward import (attention_backward, attention_backward_dq_rows, output_gradient_rowsum,
                        softmax_jacobian_product)
-from . import scalar
+from . import rope, scalar
 
 __all__ = [
     "attention",
@@ -41,6 +44,7 @@ __all__ = [
     "flash_forward",
     "merge",
     "scalar",
+    "rope",
     "attention_backward",
     "attention_backward_dq_rows",
     "output_gradient_rowsum",
