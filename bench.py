@@ -138,10 +138,173 @@ def copy_calibration(torch, mib: int) -> int:
     return 0
 
 
+def time_calls(torch, step, warmup: int, steps: int):
+    """Warm-up calls, then `steps` timed calls: (wall ms per call over the timed region, list
+    of per-call HIP-event ms recorded on torch's current stream, where libfa launches)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
+
+
+def rope_tables(positions: int, head_dim: int, base: float = 10000.0):
+    """Standard RoPE tables, fp32 [positions, head_dim / 2]: cos and sin of p * base^(-2i/d)."""
+    inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def bits(t, torch) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_leg(kind: str, w: si.Workload, inp: si.Inputs, gpu: dict, args) -> dict:
+    """The CPU baseline (the oracle timed on a bounded sample) and a quick parity check of
+    seeded rows of the GPU result against the oracle: the only part of the bench that runs
+    the oracle."""
+    import oracle
+    import oracle.rope
+
+    out = {"cpu_baseline": cpu_baseline(w, inp, args.cpu_seconds, bytes_metric=(kind == "splitkv"))}
+    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    if kind == "backward":
+        rows = si.sample_rows(w, 0.0, seed=8, max_rows=32)
+        dof = si.bits_to_f64(gpu["dout_bits"], w.dtype).astype(np.float32)
+        dq_ref = oracle.attention_backward_dq_rows(qf, kf, vf, dof, w.scale, w.causal, rows,
+                                                   cu_seqlens=inp.cu_seqlens)
+        idx = tuple(np.array(rows).T)
+        dq_gpu = si.bits_to_f64(gpu["dq_bits"][idx], w.dtype)
+        out["parity"] = {"dq_rows": len(rows), "max_abs_ddQ": float(np.abs(dq_gpu - dq_ref).max()),
+                         "max_abs_dQ_ref": float(np.abs(dq_ref).max())}
+        return out
+    rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
+    if "rope" in gpu:
+        cos, sin, inter = gpu["rope"]
+        o_ref, lse_ref = oracle.rope.attention_rope_rows(
+            qf, kf, vf, cos, sin, inter, "bf16" if w.dtype == si.BF16 else "f16", w.scale,
+            w.causal, rows, cu_seqlens=inp.cu_seqlens, cu_seqlens_k=inp.cu_seqlens_k)
+    else:
+        o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
+                                               cu_seqlens=inp.cu_seqlens,
+                                               cu_seqlens_k=inp.cu_seqlens_k)
+    idx = tuple(np.array(rows).T)
+    o_gpu = si.bits_to_f64(gpu["o_bits"][idx], w.dtype)
+    lse_gpu = gpu["lse"][idx]
+    out["parity"] = {
+        "rows": len(rows),
+        "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
+        "max_lse_err": float((np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1)).max()),
+    }
+    return out
+
+
+def common_line(args, w: si.Workload, metric: str, value: float, unit: str, ms_per_step: float):
+    return {
+        "metric": metric,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, see seeded_inputs.py)",
+    }
+
+
+def workload_config(w: si.Workload) -> dict:
+    return {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+            "seqlen": w.seqlen, "seqlen_k": w.keys, "head_dim": w.head_dim, "causal": w.causal,
+            "num_seqs": len(w.seq_lens) if w.varlen else None}
+
+
+def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> int:
+    """fa_fwd over the workload; with --rope, RoPE on Q (as it is loaded) and K (the key pass)."""
+    dev = q.device
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
+    cu_k = torch.from_numpy(inp.cu_seqlens_k).to(dev) if inp.cu_seqlens_k is not None else None
+    max_seqlen = w.max_seqlen() if w.varlen else None
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    kw = dict(scale=w.scale, causal=w.causal, cu_seqlens=cu, max_seqlen=max_seqlen,
+              cu_seqlens_k=cu_k)
+    gpu = {}
+    if args.rope:
+        cos, sin = rope_tables(max(w.keys, 1), w.head_dim)
+        gpu["rope"] = (cos, sin, False)
+        kw.update(rope_cos=torch.from_numpy(cos).to(dev), rope_sin=torch.from_numpy(sin).to(dev))
+        k_rot = torch.empty_like(k)
+
+        def step():
+            fa.fa_fwd(q, k, v, o, lse, k_rot=k_rot, **kw)
+
+        def kernel_only():  # the attention kernel alone: keys already rotated, Q rotated on load
+            fa.fa_fwd(q, k_rot, v, o, lse, **kw)
+    else:
+        def step():
+            fa.fa_fwd(q, k, v, o, lse, **kw)
+        kernel_only = step
+
+    ms_per_step, launch_ms = time_calls(torch, step, args.warmup, args.steps)
+    if kernel_only is not step:
+        _, kernel_ms = time_calls(torch, kernel_only, 3, args.steps)
+        step()  # leaves o, lse from the full call
+        torch.cuda.synchronize()
+    else:
+        kernel_ms = launch_ms
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    metric = METRIC if (w.name == si.HEADLINE and not args.rope) else (
+        f"attention fwd TFLOP/s and % of MFMA peak, {w.name}" + (" + RoPE" if args.rope else ""))
+    line = common_line(args, w, metric, round(value, 2), "TFLOP/s", ms_per_step)
+    line["config"] = {**workload_config(w), "flop_count": flops,
+                      "flop_convention": ("4*N^2*d per (batch, head), halved for causal"
+                                          if w.seqlen_k is None else
+                                          "4*Nq*Nk*d per (batch, head), less 2*Nq^2*d for causal")}
+    if args.rope:
+        line["config"]["rope"] = ("half-split pairs, standard tables; K rotated by the key pass, "
+                                  "Q as it is loaded")
+    line["pct_of_peak"] = round(100.0 * value / peak, 2)
+    line["roofline"] = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None if args.rope else measured_traffic(w.name),
+        "kernel": "fa_fwd_kernel",
+        "avg_launch_ms": round(avg_kernel_ms, 4),
+        "launch_ms_min_max": [round(min(kernel_ms), 4), round(max(kernel_ms), 4)],
+    }
+    if args.rope:
+        line["roofline"]["avg_call_ms_with_key_pass"] = round(float(np.mean(launch_ms)), 4)
+    line["kernel_source_sha256"] = kernel_source_hash()
+    if not args.no_cpu_baseline:
+        gpu.update(o_bits=bits(o, torch), lse=lse.cpu().numpy().astype(np.float64))
+        line.update(oracle_leg("forward", w, inp, gpu, args))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up) -> int:
     """The backward pass (delta, dK/dV and dQ kernels) of a self-attention workload."""
-    import oracle
-
     if w.seqlen_k is not None:
         print("the backward pass covers self-attention workloads only", file=sys.stderr)
         return 2
@@ -159,71 +322,32 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
         fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, scale=w.scale, causal=w.causal,
                   cu_seqlens=cu, max_seqlen=max_seqlen)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in events:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    launch_ms = [a.elapsed_time(b) for a, b in events]
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, launch_ms = time_calls(torch, step, args.warmup, args.steps)
     flops = 2.5 * w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     avg_ms = float(np.mean(launch_ms))
     peak = MFMA_PEAK_TFLOPS[w.dtype]
-
-    # sampled dQ rows against the oracle (each dQ row depends on its own row only)
-    rows = si.sample_rows(w, 0.0, seed=8, max_rows=32)
-    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
-    dof = si.bits_to_f64(dout_bits, w.dtype).astype(np.float32)
-    dq_ref = oracle.attention_backward_dq_rows(qf, kf, vf, dof, w.scale, w.causal, rows,
-                                               cu_seqlens=inp.cu_seqlens)
-    idx = tuple(np.array(rows).T)
-    dq_gpu = si.bits_to_f64(dq.view(torch.int16).cpu().numpy().view(np.uint16)[idx], w.dtype)
-    line = {
-        "metric": f"attention bwd TFLOP/s and % of MFMA peak, {w.name}",
-        "value": round(value, 2),
+    line = common_line(args, w, f"attention bwd TFLOP/s and % of MFMA peak, {w.name}",
+                       round(value, 2), "TFLOP/s", ms_per_step)
+    line["data"] = "synthetic (seeded N(0,1) inputs and output gradient, see seeded_inputs.py)"
+    line["config"] = {**workload_config(w), "flop_count": flops,
+                      "flop_convention": ("2.5 x the forward's convention: 5 products (S, dP, dV, "
+                                          "dK, dQ); the kernels run 7 (S and dP again for dQ)")}
+    line["pct_of_peak"] = round(100.0 * value / peak, 2)
+    line["roofline"] = {
+        "bound": "mfma",
+        "achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+        "peak": peak,
         "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs and output gradient, see seeded_inputs.py)",
-        "config": {
-            "workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
-            "seqlen": w.seqlen, "head_dim": w.head_dim, "causal": w.causal,
-            "flop_count": flops,
-            "flop_convention": ("2.5 x the forward's convention: 5 products (S, dP, dV, dK, dQ); "
-                                "the kernels run 7 (S and dP again for dQ)"),
-        },
-        "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(flops / (avg_ms * 1e-3) / 1e12 / peak, 4),
-            "traffic": None,
-            "kernel": "fa_bwd (fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, fa_bwd_dq_kernel)",
-            "avg_launch_ms": round(avg_ms, 4),
-            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
-        },
-        "parity": {"dq_rows": len(rows),
-                   "max_abs_ddQ": float(np.abs(dq_gpu - dq_ref).max()),
-                   "max_abs_dQ_ref": float(np.abs(dq_ref).max())},
+        "frac": round(flops / (avg_ms * 1e-3) / 1e12 / peak, 4),
+        "traffic": None,
+        "kernel": "fa_bwd (fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, fa_bwd_dq_kernel)",
+        "avg_launch_ms": round(avg_ms, 4),
+        "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
     }
+    if not args.no_cpu_baseline:
+        line.update(oracle_leg("backward", w, inp, {"dout_bits": dout_bits,
+                                                    "dq_bits": bits(dq, torch)}, args))
     print(json.dumps(line), flush=True)
     return 0
 
@@ -231,8 +355,6 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
 def bench_splitkv(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> int:
     """The split-KV forward (split and merge kernels) of a decode workload, in GB/s of the
     bytes it must move."""
-    import oracle
-
     dev = q.device
     cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
     cu_k = torch.from_numpy(inp.cu_seqlens_k).to(dev) if inp.cu_seqlens_k is not None else None
@@ -247,76 +369,31 @@ def bench_splitkv(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
         fa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale=w.scale, causal=w.causal, num_splits=0,
                           cu_seqlens=cu, max_seqlen=max_seqlen, cu_seqlens_k=cu_k)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in events:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    launch_ms = [a.elapsed_time(b) for a, b in events]
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, launch_ms = time_calls(torch, step, args.warmup, args.steps)
     nbytes = w.io_bytes()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     avg_ms = float(np.mean(launch_ms))
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
-
-    rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
-    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
-    o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
-                                           cu_seqlens=inp.cu_seqlens,
-                                           cu_seqlens_k=inp.cu_seqlens_k)
-    del qf, kf, vf
-    idx = tuple(np.array(rows).T)
-    o_gpu = si.bits_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16)[idx], w.dtype)
-    lse_gpu = lse.cpu().numpy().astype(np.float64)[idx]
-    line = {
-        "metric": f"attention decode GB/s (Q, K, V read, O, LSE written), {w.name}",
-        "value": round(value, 1),
+    line = common_line(args, w, f"attention decode GB/s (Q, K, V read, O, LSE written), {w.name}",
+                       round(value, 1), "GB/s", ms_per_step)
+    line["config"] = {**workload_config(w), "splits": splits, "workspace_bytes": ws_bytes,
+                      "io_bytes": nbytes}
+    line["roofline"] = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs, see seeded_inputs.py)",
-        "config": {
-            "workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
-            "seqlen": w.seqlen, "seqlen_k": w.keys, "head_dim": w.head_dim, "causal": w.causal,
-            "num_seqs": len(w.seq_lens) if w.varlen else None, "splits": splits,
-            "workspace_bytes": ws_bytes, "io_bytes": nbytes,
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(w.name, "fa_splitkv"),
-            "kernel": "fa_fwd_splitkv (fa_splitkv_kernel + fa_splitkv_merge_kernel)",
-            "avg_launch_ms": round(avg_ms, 4),
-            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
-        },
-        "parity": {
-            "rows": len(rows),
-            "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
-            "max_lse_err": float((np.abs(lse_gpu - lse_ref)
-                                  / np.maximum(np.abs(lse_ref), 1)).max()),
-        },
-        "kernel_source_sha256": kernel_source_hash(SPLITKV_SOURCES),
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": measured_traffic(w.name, "fa_splitkv"),
+        "kernel": "fa_fwd_splitkv (fa_splitkv_kernel + fa_splitkv_merge_kernel)",
+        "avg_launch_ms": round(avg_ms, 4),
+        "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
     }
+    line["kernel_source_sha256"] = kernel_source_hash(SPLITKV_SOURCES)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, bytes_metric=True)
+        line.update(oracle_leg("splitkv", w, inp, {"o_bits": bits(o, torch),
+                                                   "lse": lse.cpu().numpy().astype(np.float64)},
+                               args))
     print(json.dumps(line), flush=True)
     return 0
 
@@ -329,6 +406,9 @@ def main() -> int:
     ap.add_argument("--workload", default=si.HEADLINE, choices=si.WORKLOAD_ORDER)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", action="store_true",
+                    help="forward with rotary position embedding (standard tables, half-split "
+                         "pairs): Q rotated as it is loaded, K by the key pass")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -365,100 +445,7 @@ def main() -> int:
         return bench_backward(args, torch, fa, w, inp, q, k, v, up)
     if w.splitkv:
         return bench_splitkv(args, torch, fa, w, inp, q, k, v)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    cu = torch.from_numpy(inp.cu_seqlens).to(dev) if w.varlen else None
-    max_seqlen = w.max_seqlen() if w.varlen else None
-
-    def step():
-        fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal, cu_seqlens=cu,
-                  max_seqlen=max_seqlen)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()  # fa_fwd launches on this stream
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in events:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    launch_ms = [a.elapsed_time(b) for a, b in events]
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    flops = w.flops()
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    avg_launch_ms = float(np.mean(launch_ms))
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    peak = MFMA_PEAK_TFLOPS[w.dtype]
-
-    # quick parity on a few seeded rows (the tests cover parity in depth)
-    import oracle
-    rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
-    qf, kf, vf = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
-    o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows,
-                                           cu_seqlens=inp.cu_seqlens)
-    del qf, kf, vf
-    idx = tuple(np.array(rows).T)
-    o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
-    o_gpu = si.bits_to_f64(o_bits[idx], w.dtype)
-    lse_gpu = lse.cpu().numpy().astype(np.float64)[idx]
-    parity = {
-        "rows": len(rows),
-        "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
-        "max_lse_err": float((np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1)).max()),
-    }
-
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) inputs, see seeded_inputs.py)",
-        "config": {
-            "workload": w.name,
-            "batch": w.batch,
-            "heads_q": w.heads_q,
-            "heads_kv": w.heads_kv,
-            "seqlen": w.seqlen,
-            "seqlen_k": w.keys,
-            "head_dim": w.head_dim,
-            "causal": w.causal,
-            "flop_count": flops,
-            "flop_convention": ("4*N^2*d per (batch, head), halved for causal"
-                                if w.seqlen_k is None else
-                                "4*Nq*Nk*d per (batch, head), less 2*Nq^2*d for causal"),
-        },
-        "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(w.name),
-            "kernel": "fa_fwd_kernel",
-            "avg_launch_ms": round(avg_launch_ms, 4),
-            "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
-        },
-        "parity": parity,
-        "kernel_source_sha256": kernel_source_hash(),
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
-    return 0
+    return bench_forward(args, torch, fa, w, inp, q, k, v)
 
 
 if __name__ == "__main__":

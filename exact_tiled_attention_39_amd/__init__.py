@@ -26,7 +26,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 FA_F16, FA_BF16 = 0, 1
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 4
+FA_ABI_VERSION = 5
 FA_MAX_SPLITS = 256
 
 _I64x3 = ctypes.c_int64 * 3
@@ -60,6 +60,12 @@ class FaFwdParams(ctypes.Structure):
         ("seqlen_k", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
         ("cu_seqlens_k", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p),
+        ("rope_sin", ctypes.c_void_p),
+        ("rope_rows", ctypes.c_int32),
+        ("rope_interleaved", ctypes.c_int32),
+        ("k_rot", ctypes.c_void_p),
+        ("k_rot_stride", _I64x3),
     ]
 
     def __init__(self, **kw):
@@ -199,9 +205,13 @@ def _strides(t: torch.Tensor):
 def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                 lse: torch.Tensor, scale: float, causal: bool,
                 cu_seqlens: Optional[torch.Tensor], max_seqlen: Optional[int],
-                cu_seqlens_k: Optional[torch.Tensor] = None) -> FaFwdParams:
+                cu_seqlens_k: Optional[torch.Tensor] = None,
+                rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+                rope_interleaved: bool = False,
+                k_rot: Optional[torch.Tensor] = None) -> FaFwdParams:
     """Fills FaFwdParams from [B, H, N, d] tensors (strides in elements); K and V may have
-    their own token count."""
+    their own token count. RoPE: contiguous fp32 tables [positions, d/2], and k_rot (shaped
+    like k) to receive the rotated keys, or None when k already holds rotated keys."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v and o must be 4-D [batch, heads, tokens, head_dim]")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
@@ -241,6 +251,28 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
         if cu_seqlens_k.device != q.device:
             raise ValueError("cu_seqlens_k must live on the same device as q")
         p.cu_seqlens_k = cu_seqlens_k.data_ptr()
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin go together")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if (t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != d // 2
+                    or not t.is_contiguous() or t.device != q.device):
+                raise ValueError(f"{name} must be a contiguous float32 [positions, head_dim/2] "
+                                 "tensor on the device of q")
+        if rope_sin.shape != rope_cos.shape:
+            raise ValueError("rope_cos and rope_sin must have one shape")
+        p.rope_cos, p.rope_sin = rope_cos.data_ptr(), rope_sin.data_ptr()
+        p.rope_rows = rope_cos.shape[0]
+        p.rope_interleaved = int(bool(rope_interleaved))
+        if k_rot is not None:
+            if (k_rot.shape != k.shape or k_rot.dtype != k.dtype or k_rot.device != q.device
+                    or (k_rot.stride(3) != 1 and k_rot.numel() > 0)):
+                raise ValueError("k_rot must be shaped like k, on its device, with head_dim "
+                                 "contiguous")
+            p.k_rot = k_rot.data_ptr()
+            p.k_rot_stride = _strides(k_rot)
+    elif k_rot is not None:
+        raise ValueError("k_rot needs the RoPE tables")
     return p
 
 
@@ -248,13 +280,17 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
            lse: torch.Tensor, *, scale: float, causal: bool = False,
            cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
            stream: Optional[torch.cuda.Stream] = None,
-           cu_seqlens_k: Optional[torch.Tensor] = None) -> None:
-    """Enqueues the forward pass writing o and lse, on `stream` (default: torch's current)."""
+           cu_seqlens_k: Optional[torch.Tensor] = None,
+           rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+           rope_interleaved: bool = False, k_rot: Optional[torch.Tensor] = None) -> None:
+    """Enqueues the forward pass writing o and lse, on `stream` (default: torch's current);
+    with RoPE tables also the rotated keys into k_rot (None: k is already rotated)."""
     lib = load_library()
     for t in (q, k, v, o, lse):
         if not t.is_cuda:
             raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
-    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k,
+                    rope_cos, rope_sin, rope_interleaved, k_rot)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         st = int(lib.fa_fwd(ctypes.byref(p), ctypes.c_void_p(s.cuda_stream)))
@@ -262,18 +298,29 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise FaError(st, fa_status_string(st))
 
 
+def _rope_keys_out(k: torch.Tensor, rope_cos, keys_rotated: bool):
+    """The buffer the rotated keys go to: None without RoPE or when k is already rotated."""
+    if rope_cos is None or keys_rotated:
+        return None
+    return torch.empty(k.shape, dtype=k.dtype, device=k.device)
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
               scale: Optional[float] = None, causal: bool = False,
               cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
-              cu_seqlens_k: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, torch.Tensor]:
+              cu_seqlens_k: Optional[torch.Tensor] = None,
+              rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+              rope_interleaved: bool = False, keys_rotated: bool = False,
+              return_k_rot: bool = False):
     """softmax(scale * Q K^T) V and its per-row log-sum-exp, for [B, H, N, d] tensors.
 
     scale defaults to 1/sqrt(d). K and V may hold more (or fewer) tokens than Q: the queries
     are then the last positions of the keys, which is what causal masking measures from. With
     cu_seqlens (int32 prefix sums, batch 1) sequences are packed along the token axis and
     attend only within themselves (keys per cu_seqlens_k when packed differently); max_seqlen,
-    if omitted, is read from cu_seqlens with a device-to-host copy.
+    if omitted, is read from cu_seqlens with a device-to-host copy. With RoPE tables (fp32
+    [positions, d/2] cos and sin) Q and K are rotated by their positions first; keys_rotated
+    says K already holds rotated keys, and return_k_rot also returns the rotated keys.
     """
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
@@ -282,9 +329,11 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
         max_seqlen = int(lens.max()) if lens.numel() else 0
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    k_rot = _rope_keys_out(k, rope_cos, keys_rotated)
     fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
-           max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k)
-    return o, lse
+           max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k, rope_cos=rope_cos,
+           rope_sin=rope_sin, rope_interleaved=rope_interleaved, k_rot=k_rot)
+    return (o, lse, k_rot) if return_k_rot else (o, lse)
 
 
 def fa_splitkv_plan(params: FaFwdParams, num_splits: int = 0) -> Tuple[int, int]:
@@ -303,14 +352,18 @@ def fa_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
                    causal: bool = False, num_splits: int = 0,
                    cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
                    stream: Optional[torch.cuda.Stream] = None,
-                   cu_seqlens_k: Optional[torch.Tensor] = None) -> None:
+                   cu_seqlens_k: Optional[torch.Tensor] = None,
+                   rope_cos: Optional[torch.Tensor] = None,
+                   rope_sin: Optional[torch.Tensor] = None, rope_interleaved: bool = False,
+                   k_rot: Optional[torch.Tensor] = None) -> None:
     """Enqueues the split-KV forward writing o and lse; `workspace` is a device tensor of at
     least fa_splitkv_plan's byte count (None when that is 0)."""
     lib = load_library()
     for t in (q, k, v, o, lse) + ((workspace,) if workspace is not None else ()):
         if not t.is_cuda:
             raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
-    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k,
+                    rope_cos, rope_sin, rope_interleaved, k_rot)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         if not workspace.is_contiguous():
@@ -328,8 +381,10 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                       scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
                       cu_seqlens: Optional[torch.Tensor] = None,
                       max_seqlen: Optional[int] = None,
-                      cu_seqlens_k: Optional[torch.Tensor] = None
-                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+                      cu_seqlens_k: Optional[torch.Tensor] = None,
+                      rope_cos: Optional[torch.Tensor] = None,
+                      rope_sin: Optional[torch.Tensor] = None, rope_interleaved: bool = False,
+                      keys_rotated: bool = False, return_k_rot: bool = False):
     """``attention`` computed by the split-KV kernels (meant for a few queries per sequence
     against many keys); allocates O, LSE and the workspace."""
     if scale is None:
@@ -339,12 +394,16 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
         max_seqlen = int(lens.max()) if lens.numel() else 0
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k)
+    k_rot = _rope_keys_out(k, rope_cos, keys_rotated)
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k,
+                    rope_cos, rope_sin, rope_interleaved, k_rot)
     _, nbytes = fa_splitkv_plan(p, num_splits)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     fa_fwd_splitkv(q, k, v, o, lse, ws, scale=scale, causal=causal, num_splits=num_splits,
-                   cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k)
-    return o, lse
+                   cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k,
+                   rope_cos=rope_cos, rope_sin=rope_sin, rope_interleaved=rope_interleaved,
+                   k_rot=k_rot)
+    return (o, lse, k_rot) if return_k_rot else (o, lse)
 
 
 def make_bwd_params(q, k, v, o, dout, lse, dq, dk, dv, delta, scale: float, causal: bool,

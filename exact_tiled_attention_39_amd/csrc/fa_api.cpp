@@ -67,6 +67,21 @@ fa_status fa_check_args(const fa_fwd_params* p) {
       !stride_ok(p->v_stride, p->head_dim, p->seqlen_k) ||
       !stride_ok(p->o_stride, p->head_dim, p->seqlen))
     return FA_ERR_ALIGN;
+  if ((p->rope_cos == nullptr) != (p->rope_sin == nullptr)) return FA_ERR_NULL;
+  if (p->rope_cos == nullptr) {
+    if (p->k_rot != nullptr) return FA_ERR_NULL;
+  } else {
+    if (!aligned16(p->rope_cos) || !aligned16(p->rope_sin)) return FA_ERR_ALIGN;
+    if (p->rope_rows < 1) return FA_ERR_SHAPE;
+    if (p->cu_seqlens == nullptr && p->rope_rows < p->seqlen_k) return FA_ERR_SHAPE;
+    if (p->k_rot != nullptr &&
+        (!aligned16(p->k_rot) || !stride_ok(p->k_rot_stride, p->head_dim, p->seqlen_k)))
+      return FA_ERR_ALIGN;
+    // the key rotation runs one thread per 16 head-dims of every key row
+    if (p->k_rot != nullptr &&
+        product_exceeds(p->batch, p->heads_kv, p->seqlen_k, int64_t(UINT32_MAX) * 16))
+      return FA_ERR_SHAPE;
+  }
   // The kernel runs one workgroup per (256 query rows, query head, batch entry or sequence);
   // the bound below counts 128-row blocks, so it is conservative.
   const int64_t rows = p->cu_seqlens ? p->max_seqlen : p->seqlen;

@@ -141,5 +141,72 @@ struct TransposeLayout {
   }
 };
 
+// RoPE rotation of one pair by (c, s): (a c - b s, a s + b c), each product and the sum or
+// difference rounded to fp32 on its own (no fused multiply-add), as the library documents.
+__device__ __forceinline__ void rope_pair(float a, float b, float c, float s, float& ra,
+                                          float& rb) {
+#pragma clang fp contract(off)
+  const float ac = a * c;
+  const float bs = b * s;
+  const float as = a * s;
+  const float bc = b * c;
+  ra = ac - bs;
+  rb = as + bc;
+}
+
+// Rotates one row held as MFMA operand fragments in place: fragment t holds the 8 elements at
+// head-dims 16 t + 8 half .. + 7 (the operand layout of the Q^T B operand). cs and sn point at
+// the fp32 table row of the row's position. Interleaved pairs (2i, 2i + 1) lie inside one
+// fragment; half-split pairs (i, i + D/2) are fragments t and t + kSteps / 2 of the same lane.
+template <bool BF16, int kSteps>
+__device__ __forceinline__ void rope_rotate_fragments(u32x4 (&x)[kSteps], const float* cs,
+                                                      const float* sn, bool interleaved,
+                                                      int half) {
+  using E = Elem<BF16>;
+  auto unpack = [](u32x4 v, float (&f)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[2 * w] = E::to_f32(uint16_t(v[w] & 0xFFFFu));
+      f[2 * w + 1] = E::to_f32(uint16_t(v[w] >> 16));
+    }
+  };
+  auto pack = [](const float (&f)[8]) __attribute__((always_inline)) {
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = E::pack(f[2 * w], f[2 * w + 1]);
+    return v;
+  };
+  if (interleaved) {
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const int f0 = 8 * t + 4 * half;  // frequencies of the fragment's 4 pairs
+      const f32x4 c = *reinterpret_cast<const f32x4*>(cs + f0);
+      const f32x4 s = *reinterpret_cast<const f32x4*>(sn + f0);
+      float e[8];
+      unpack(x[t], e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rope_pair(e[2 * i], e[2 * i + 1], c[i], s[i], e[2 * i], e[2 * i + 1]);
+      x[t] = pack(e);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kSteps / 2; ++t) {
+      const int f0 = 16 * t + 8 * half;  // frequencies of the fragment's 8 elements
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + f0);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + f0 + 4);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(sn + f0);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(sn + f0 + 4);
+      float a[8], b[8];
+      unpack(x[t], a);
+      unpack(x[t + kSteps / 2], b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rope_pair(a[i], b[i], i < 4 ? c0[i] : c1[i - 4], i < 4 ? s0[i] : s1[i - 4], a[i], b[i]);
+      x[t] = pack(a);
+      x[t + kSteps / 2] = pack(b);
+    }
+  }
+}
+
 }  // namespace dev
 }  // namespace fa

@@ -80,6 +80,10 @@ struct KernelArgs {
   uint32_t q_xor;     // 0x80008000 when scale < 0: Q is negated exactly and c stays positive
   int32_t xcd_group;  // 0: plain order; 1: (batch, head) pairs in 8 contiguous runs, one per
                       // XCD; 2: kv heads dealt to the 8 XCDs in turn (heads_kv % 8 == 0)
+  const float* rope_cos;  // RoPE tables [rope_rows, D / 2], or NULL: Q is not rotated
+  const float* rope_sin;
+  int32_t rope_rows;
+  int32_t rope_interleaved;
 };
 
 // Fragment-major tile geometry. A K tile is kKBlocks blocks of 1 KB, block (kb, s) holding
@@ -208,6 +212,14 @@ void fa_fwd_kernel(const KernelArgs p) {
     for (int s = 0; s < kSteps; ++s)
       qf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + s * 32,
                                                                               0, 0));
+    if (p.rope_cos != nullptr) {
+      // RoPE: the lane's query row sits at key position qrow + shift (rows outside the
+      // sequence hold zeros; their position is clamped only to stay inside the tables)
+      const int pos = min(max(qrow + shift, 0), p.rope_rows - 1);
+      rope_rotate_fragments<BF16, kSteps>(qf, p.rope_cos + int64_t(pos) * (D / 2),
+                                          p.rope_sin + int64_t(pos) * (D / 2),
+                                          p.rope_interleaved != 0, half);
+    }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) qf[s] = (qf[s] & p.q_and) ^ p.q_xor;
   }
@@ -515,6 +527,10 @@ hipError_t launch_mode(const KernelArgs& a, int grid, bool causal, bool varlen,
 }  // namespace
 
 fa_status launch_forward(const fa_fwd_params& p, void* stream, const char** hip_error) {
+  if (p.rope_cos != nullptr && p.k_rot != nullptr) {
+    const fa_status st = launch_rope_keys(p, stream, hip_error);
+    if (st != FA_OK) return st;
+  }
   KernelArgs a;
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
@@ -527,6 +543,14 @@ fa_status launch_forward(const fa_fwd_params& p, void* stream, const char** hip_
   a.k_sb = p.k_stride[0]; a.k_sh = p.k_stride[1]; a.k_sn = p.k_stride[2];
   a.v_sb = p.v_stride[0]; a.v_sh = p.v_stride[1]; a.v_sn = p.v_stride[2];
   a.o_sb = p.o_stride[0]; a.o_sh = p.o_stride[1]; a.o_sn = p.o_stride[2];
+  if (p.rope_cos != nullptr && p.k_rot != nullptr) {  // attention reads the rotated keys
+    a.k = static_cast<const uint16_t*>(p.k_rot);
+    a.k_sb = p.k_rot_stride[0]; a.k_sh = p.k_rot_stride[1]; a.k_sn = p.k_rot_stride[2];
+  }
+  a.rope_cos = p.rope_cos;
+  a.rope_sin = p.rope_sin;
+  a.rope_rows = p.rope_rows;
+  a.rope_interleaved = p.rope_interleaved;
   a.seqlen = p.seqlen;
   a.seqlen_k = p.seqlen_k;
   a.heads_q = p.heads_q;

@@ -69,6 +69,10 @@ struct SplitArgs {
   float c;              // |scale| * log2(e), or log2(e) when scale == 0
   uint32_t q_and;       // 0 when scale == 0, else all ones
   uint32_t q_xor;       // 0x80008000 when scale < 0 (Q negated exactly)
+  const float* rope_cos;  // RoPE tables [rope_rows, D / 2], or NULL: Q is not rotated
+  const float* rope_sin;
+  int32_t rope_rows;
+  int32_t rope_interleaved;
 };
 
 template <int D>
@@ -143,6 +147,13 @@ void fa_splitkv_kernel(const SplitArgs p) {
   } else {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) qf[s] = u32x4{0, 0, 0, 0};
+  }
+  if (p.rope_cos != nullptr) {
+    // RoPE: query token tq sits at key position tq + shift (clamped into the tables)
+    const int pos = min(max(tq + shift, 0), p.rope_rows - 1);
+    rope_rotate_fragments<BF16, kSteps>(qf, p.rope_cos + int64_t(pos) * (D / 2),
+                                        p.rope_sin + int64_t(pos) * (D / 2),
+                                        p.rope_interleaved != 0, half);
   }
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) qf[s] = (qf[s] & p.q_and) ^ p.q_xor;
@@ -421,6 +432,10 @@ SplitPlan plan_splitkv(const fa_fwd_params& p, int32_t num_splits) {
 
 fa_status launch_forward_splitkv(const fa_fwd_params& p, const SplitPlan& plan, void* workspace,
                                  void* stream, const char** hip_error) {
+  if (p.rope_cos != nullptr && p.k_rot != nullptr) {
+    const fa_status st = launch_rope_keys(p, stream, hip_error);
+    if (st != FA_OK) return st;
+  }
   SplitArgs a;
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
@@ -436,6 +451,14 @@ fa_status launch_forward_splitkv(const fa_fwd_params& p, const SplitPlan& plan, 
   a.k_sb = p.k_stride[0]; a.k_sh = p.k_stride[1]; a.k_sn = p.k_stride[2];
   a.v_sb = p.v_stride[0]; a.v_sh = p.v_stride[1]; a.v_sn = p.v_stride[2];
   a.o_sb = p.o_stride[0]; a.o_sh = p.o_stride[1]; a.o_sn = p.o_stride[2];
+  if (p.rope_cos != nullptr && p.k_rot != nullptr) {  // attention reads the rotated keys
+    a.k = static_cast<const uint16_t*>(p.k_rot);
+    a.k_sb = p.k_rot_stride[0]; a.k_sh = p.k_rot_stride[1]; a.k_sn = p.k_rot_stride[2];
+  }
+  a.rope_cos = p.rope_cos;
+  a.rope_sin = p.rope_sin;
+  a.rope_rows = p.rope_rows;
+  a.rope_interleaved = p.rope_interleaved;
   a.rows_total = plan.rows_total;
   a.seqlen = p.seqlen;
   a.seqlen_k = p.seqlen_k;

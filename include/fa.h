@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -115,7 +115,37 @@ typedef struct fa_fwd_params {
                                   k, v may be NULL */
   int32_t reserved0;           /* must be 0 */
   const int32_t* cu_seqlens_k; /* packed key ranges, or NULL (see above) */
+  /* since ABI version 5: rotary position embedding (RoPE, see below) */
+  const float* rope_cos;       /* NULL: no rotation; else fp32 [rope_rows, head_dim / 2] */
+  const float* rope_sin;       /* fp32 [rope_rows, head_dim / 2]; both or neither */
+  int32_t rope_rows;           /* positions the tables hold (rows are 16-byte aligned) */
+  int32_t rope_interleaved;    /* non-zero: pairs (2i, 2i + 1); zero: pairs (i, i + head_dim/2) */
+  void* k_rot;                 /* NULL: K holds keys that are already rotated; else the rotated
+                                  keys are written here ([batch, heads_kv, seqlen_k, head_dim]
+                                  with k_rot_stride; may be k itself with k's strides) and
+                                  attention reads them */
+  int64_t k_rot_stride[3];
 } fa_fwd_params;
+
+/*
+ * RoPE. The "Flash Attention" notes list rotary position embedding among FlashAttention-2's
+ * features ("Flash Attention 2 Improvements"). With rope_cos and rope_sin given, attention runs
+ * on rotated Q and K: pair i of a row at position p becomes (a c - b s, a s + b c) with
+ * c = rope_cos[p][i], s = rope_sin[p][i] (the standard tables hold cos and sin of
+ * p * 10000^(-2i/head_dim); any tables are accepted). Positions count inside each sequence:
+ * key j is at position j, and the queries are the last positions of the keys (query t of Nq
+ * against Nk keys at Nk - Nq + t; below 0 taken as 0), so the causal alignment and the rotation
+ * agree. Each rotated element is formed in fp32 as two rounded products and their rounded
+ * difference or sum (no fused multiply-add), then rounded to the input type (round to nearest
+ * even). Q is rotated as it is loaded; K is rotated once by a separate streaming kernel into
+ * k_rot (each key tile is read by many query blocks, so rotating it there would repeat the
+ * work), unless k_rot is NULL, in which case K is taken as already rotated (a cache of rotated
+ * keys). Table rows must cover every key position: with cu_seqlens this is the caller's promise
+ * (positions beyond the tables use the last row; nothing is read out of bounds), otherwise
+ * rope_rows >= seqlen_k is checked. Errors: FA_ERR_NULL for one table without the other or
+ * k_rot without tables; FA_ERR_ALIGN for a table not 16-byte aligned or a bad k_rot layout;
+ * FA_ERR_SHAPE for too few table rows. The backward pass takes no RoPE arguments.
+ */
 
 /*
  * Arguments of one backward call: the gradients dQ, dK, dV of the loss sum(O * dO) for the

@@ -38,11 +38,15 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_layout():
     assert fa.fa_abi_version() == fa.FA_ABI_VERSION
-    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 208
+    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 264
     assert fa.FaFwdParams.cu_seqlens.offset == 88
     assert fa.FaFwdParams.o_stride.offset == 168
     assert fa.FaFwdParams.seqlen_k.offset == 192
     assert fa.FaFwdParams.cu_seqlens_k.offset == 200
+    assert fa.FaFwdParams.rope_cos.offset == 208
+    assert fa.FaFwdParams.rope_rows.offset == 224
+    assert fa.FaFwdParams.k_rot.offset == 232
+    assert fa.FaFwdParams.k_rot_stride.offset == 240
 
 
 ALIGNED = 0x10000
@@ -58,6 +62,9 @@ def good(**kw):
     p = fa.FaFwdParams(**{k: v for k, v in base.items() if not k.endswith("_stride")})
     for name, val in strides.items():
         setattr(p, name, fa._I64x3(*kw.get(name, val)))
+    for name, val in kw.items():
+        if name.endswith("_stride") and name not in strides:
+            setattr(p, name, fa._I64x3(*val))
     return p
 
 
@@ -112,6 +119,38 @@ def test_each_error_is_reported_before_any_device_call(kw, status):
     assert fa.fa_check_args(p) == status
     lib = fa.load_library()
     assert lib.fa_fwd(ctypes.byref(p), None) == status  # rejected before touching a device
+
+
+ROPE = dict(rope_cos=ALIGNED * 8, rope_sin=ALIGNED * 9, rope_rows=100, k_rot=ALIGNED * 10,
+            k_rot_stride=(2 * 100 * 128, 100 * 128, 128))
+
+
+def test_rope_arguments_pass():
+    assert fa.fa_check_args(good(**ROPE)) == fa.FA_OK
+    assert fa.fa_check_args(good(**{**ROPE, "k_rot": 0})) == fa.FA_OK  # keys already rotated
+    assert fa.fa_check_args(good(**{**ROPE, "k_rot": ALIGNED * 2})) == fa.FA_OK  # in place
+    # packed sequences: table coverage is the caller's promise
+    assert fa.fa_check_args(good(**{**ROPE, "rope_rows": 3}, batch=1, cu_seqlens=ALIGNED * 6,
+                                 num_seqs=3, max_seqlen=50)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rope_sin=0), fa.FA_ERR_NULL),                      # one table without the other
+    (dict(rope_cos=0, rope_sin=0), fa.FA_ERR_NULL),          # k_rot without tables
+    (dict(rope_cos=ALIGNED * 8 + 4), fa.FA_ERR_ALIGN),
+    (dict(rope_sin=ALIGNED * 9 + 8), fa.FA_ERR_ALIGN),
+    (dict(rope_rows=0), fa.FA_ERR_SHAPE),
+    (dict(rope_rows=99), fa.FA_ERR_SHAPE),                   # key positions reach 99
+    (dict(k_rot=ALIGNED * 10 + 2), fa.FA_ERR_ALIGN),
+    (dict(k_rot_stride=(0, 0, 100)), fa.FA_ERR_ALIGN),
+    (dict(k_rot_stride=(0, 0, 64)), fa.FA_ERR_ALIGN),        # overlapping rows
+])
+def test_rope_errors_before_any_device_call(kw, status):
+    p = good(**{**ROPE, **kw})
+    assert fa.fa_check_args(p) == status
+    lib = fa.load_library()
+    assert lib.fa_fwd(ctypes.byref(p), None) == status
+    assert lib.fa_fwd_splitkv(ctypes.byref(p), 1, None, 0, None) == status
 
 
 def test_struct_size_mismatch_and_null_params():
