@@ -247,6 +247,59 @@ def random_inputs(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim
                   dtype, 1.0 / math.sqrt(head_dim) if scale is None else scale, causal, cu, cu_k)
 
 
+@dataclasses.dataclass
+class Inputs8:
+    """E4M3 (OCP) codes of Q, K, V ([B, H, N, d] uint8) with one fp32 descale per (batch, head):
+    code value times descale is the tensor the code stands for."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_descale: np.ndarray  # [B, Hq]
+    k_descale: np.ndarray  # [B, Hkv]
+    v_descale: np.ndarray  # [B, Hkv]
+    scale: float
+    causal: bool
+    cu_seqlens: Optional[np.ndarray] = None
+    cu_seqlens_k: Optional[np.ndarray] = None
+
+
+def quantize_e4m3(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-(batch, head) amax scaling of a float32 [B, H, N, d] tensor to E4M3 codes: descale
+    = amax / 448 (1 for an all-zero head), codes = x / descale clamped to +-448 and rounded to
+    nearest even (storage conversion through torch's float8_e4m3fn on the CPU)."""
+    import torch
+
+    amax = np.abs(x).max(axis=(2, 3)) if x.size else np.zeros(x.shape[:2], np.float32)
+    descale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    y = np.clip(x / descale[:, :, None, None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.numpy(), descale
+
+
+def random_inputs_fp8(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int,
+                      seed: int, *, causal: bool = False, scale: Optional[float] = None,
+                      seq_lens: Optional[Tuple[int, ...]] = None, seqlen_k: Optional[int] = None,
+                      seq_lens_k: Optional[Tuple[int, ...]] = None) -> Inputs8:
+    """Q, K, V ~ N(0, 1) in float32 (the draw order of random_inputs), quantized per
+    (batch, head) to E4M3."""
+    rng = np.random.default_rng(seed)
+    nk = seqlen if seqlen_k is None else seqlen_k
+    q = rng.standard_normal((batch, heads_q, seqlen, head_dim), dtype=np.float32)
+    k = rng.standard_normal((batch, heads_kv, nk, head_dim), dtype=np.float32)
+    v = rng.standard_normal((batch, heads_kv, nk, head_dim), dtype=np.float32)
+    (qc, qd), (kc, kd), (vc, vd) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    cu = cu_k = None
+    if seq_lens is not None:
+        if batch != 1 or sum(seq_lens) != seqlen:
+            raise ValueError("packed sequences need batch == 1 and seqlen == sum(seq_lens)")
+        cu = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int32)
+    if seq_lens_k is not None:
+        cu_k = np.concatenate([[0], np.cumsum(seq_lens_k)]).astype(np.int32)
+    return Inputs8(qc, kc, vc, qd, kd, vd, 1.0 / math.sqrt(head_dim) if scale is None else scale,
+                   causal, cu, cu_k)
+
+
 def random_output_grad(inp: Inputs, seed: int) -> np.ndarray:
     """dL/dO for a backward check: N(0, 1) rounded to the dtype, shaped like Q (bit patterns)."""
     rng = np.random.default_rng(seed)

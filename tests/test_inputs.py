@@ -92,3 +92,16 @@ def test_row_sample_has_edges_and_stays_in_range():
         assert s0 in toks and s1 - 1 in toks
     assert all(0 <= t < w.seqlen and 0 <= h < w.heads_q and b == 0 for b, h, t in rows)
     assert rows == si.sample_rows(w, 1 / 4096, seed=1)
+
+
+def test_fp8_inputs_use_the_format_range_per_head():
+    a = si.random_inputs_fp8(2, 4, 2, 50, 64, seed=3, causal=True)
+    assert a.q.dtype == np.uint8 and a.q.shape == (2, 4, 50, 64) and a.k.shape == (2, 2, 50, 64)
+    assert a.q_descale.shape == (2, 4) and a.v_descale.shape == (2, 2)
+    # the largest |value| of each head maps to the largest code, 448 (0x7E / 0xFE)
+    for codes in (a.q, a.k, a.v):
+        mags = codes & 0x7F
+        assert (mags.max(axis=(2, 3)) == 0x7E).all()
+        assert (mags != 0x7F).all()  # no NaN codes
+    b = si.random_inputs_fp8(2, 4, 2, 50, 64, seed=3, causal=True)
+    np.testing.assert_array_equal(a.v, b.v)
