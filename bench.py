@@ -29,12 +29,14 @@ import seeded_inputs as si  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak, N=16K d=128 causal bf16"
 # MI355X published dense matrix peaks (TFLOP/s), per input type
-MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0}
+MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0, "e4m3": 5000.0}
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip",
                   "exact_tiled_attention_39_amd/csrc/fa_device.h"]
 SPLITKV_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_splitkv.hip",
                    "exact_tiled_attention_39_amd/csrc/fa_device.h"]
+FP8_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd_fp8.hip",
+               "exact_tiled_attention_39_amd/csrc/fa_device.h"]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -59,8 +61,8 @@ def measured_traffic(workload: str, kernel: str = "fa_fwd"):
     return float(val.group(1))
 
 
-def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float, bytes_metric: bool = False
-                 ) -> dict:
+def cpu_baseline(w: si.Workload, inp, seconds: float, bytes_metric: bool = False,
+                 arrays=None) -> dict:
     """The fp64 oracle, as it stands, on seeded query rows until the time budget is spent.
 
     Reported in TFLOP/s (4*keys*d per row), or with bytes_metric in GB/s: the rows' share of
@@ -68,7 +70,9 @@ def cpu_baseline(w: si.Workload, inp: si.Inputs, seconds: float, bytes_metric: b
     import oracle
     from threadpoolctl import threadpool_info
 
-    q, k, v = (si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    if arrays is None:
+        arrays = tuple(si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
+    q, k, v = arrays
     total_rows = w.batch * w.heads_q * w.seqlen
     if total_rows <= 4096:  # few query rows (decode): every row, in seeded order
         rows = [(b, h, t) for b in range(w.batch) for h in range(w.heads_q)
@@ -303,6 +307,71 @@ def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
     return 0
 
 
+def bench_fp8(args, torch, fa, w: si.Workload) -> int:
+    """fa_fwd on E4M3 inputs of the workload's shape (per-head amax scaling of the same seeded
+    N(0, 1) draws), bfloat16 output."""
+    inp = si.random_inputs_fp8(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, w.seed,
+                               causal=w.causal, scale=w.scale, seq_lens=w.seq_lens,
+                               seqlen_k=w.seqlen_k, seq_lens_k=w.seq_lens_k)
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    qd, kd, vd = up(inp.q_descale), up(inp.k_descale), up(inp.v_descale)
+    cu = up(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+    cu_k = up(inp.cu_seqlens_k) if inp.cu_seqlens_k is not None else None
+    max_seqlen = w.max_seqlen() if w.varlen else None
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, scale=w.scale, causal=w.causal, cu_seqlens=cu,
+                  max_seqlen=max_seqlen, cu_seqlens_k=cu_k, q_descale=qd, k_descale=kd,
+                  v_descale=vd)
+
+    ms_per_step, launch_ms = time_calls(torch, step, args.warmup, args.steps)
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    avg_ms = float(np.mean(launch_ms))
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["e4m3"]
+    line = common_line(args, w, f"attention fwd TFLOP/s and % of MFMA peak, {w.name} in FP8 E4M3",
+                       round(value, 2), "TFLOP/s", ms_per_step)
+    line["dtype"] = "e4m3"
+    line["data"] = ("synthetic (the workload's seeded N(0,1) draws, per-(batch, head) amax "
+                    "scaled to E4M3, see seeded_inputs.py)")
+    line["config"] = {**workload_config(w), "flop_count": flops, "output": "bf16",
+                      "flop_convention": "the bf16 workload's convention"}
+    line["pct_of_peak"] = round(100.0 * value / peak, 2)
+    line["roofline"] = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fa_fwd_fp8_kernel",
+        "avg_launch_ms": round(avg_ms, 4),
+        "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+    }
+    line["kernel_source_sha256"] = kernel_source_hash(FP8_SOURCES)
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.fp8
+
+        arrays = tuple(oracle.fp8.dequantize(c, d).astype(np.float32) for c, d in
+                       ((inp.q, inp.q_descale), (inp.k, inp.k_descale), (inp.v, inp.v_descale)))
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, arrays=arrays)
+        rows = si.sample_rows(w, 0.0, seed=7, max_rows=48)
+        o_ref, lse_ref = oracle.attention_rows(*arrays, w.scale, w.causal, rows,
+                                               cu_seqlens=inp.cu_seqlens,
+                                               cu_seqlens_k=inp.cu_seqlens_k)
+        idx = tuple(np.array(rows).T)
+        o_gpu = si.bits_to_f64(bits(o, torch)[idx], si.BF16)
+        lse_gpu = lse.cpu().numpy().astype(np.float64)[idx]
+        line["parity"] = {
+            "rows": len(rows), "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
+            "o_tolerance": oracle.fp8.o_tolerance(arrays[2], w.keys),
+            "max_lse_err": float((np.abs(lse_gpu - lse_ref)
+                                  / np.maximum(np.abs(lse_ref), 1)).max())}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up) -> int:
     """The backward pass (delta, dK/dV and dQ kernels) of a self-attention workload."""
     if w.seqlen_k is not None:
@@ -409,6 +478,8 @@ def main() -> int:
     ap.add_argument("--rope", action="store_true",
                     help="forward with rotary position embedding (standard tables, half-split "
                          "pairs): Q rotated as it is loaded, K by the key pass")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward on E4M3 (FP8) inputs of the workload's shape")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -434,6 +505,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = si.WORKLOADS[args.workload]
+    if args.fp8:
+        return bench_fp8(args, torch, fa, w)
     inp = si.workload_inputs(w)
     tdt = torch.bfloat16 if w.dtype == si.BF16 else torch.float16
 

@@ -10,6 +10,7 @@ The C entry points (include/fa.h) are mirrored with the same names:
 ``fa_bwd_check_args``, ``fa_status_string``, ``fa_abi_version``, ``fa_params_size``,
 ``fa_bwd_params_size``. ``attention`` allocates O and LSE and calls ``fa_fwd``;
 ``attention_splitkv`` allocates O, LSE and the split workspace and calls ``fa_fwd_splitkv``;
+``attention_fp8`` runs ``fa_fwd`` on E4M3 inputs with their descales;
 ``attention_backward`` allocates dQ, dK, dV and the delta workspace and calls ``fa_bwd``.
 """
 from __future__ import annotations
@@ -23,10 +24,10 @@ import torch  # loaded first: libfa then binds to the HIP runtime torch already 
 
 LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 
-FA_F16, FA_BF16 = 0, 1
+FA_F16, FA_BF16, FA_E4M3 = 0, 1, 2
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 5
+FA_ABI_VERSION = 6
 FA_MAX_SPLITS = 256
 
 _I64x3 = ctypes.c_int64 * 3
@@ -66,6 +67,9 @@ class FaFwdParams(ctypes.Structure):
         ("rope_interleaved", ctypes.c_int32),
         ("k_rot", ctypes.c_void_p),
         ("k_rot_stride", _I64x3),
+        ("q_descale", ctypes.c_void_p),
+        ("k_descale", ctypes.c_void_p),
+        ("v_descale", ctypes.c_void_p),
     ]
 
     def __init__(self, **kw):
@@ -193,6 +197,7 @@ def fa_bwd_check_args(params: FaBwdParams) -> int:
 
 
 _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _strides(t: torch.Tensor):
@@ -214,7 +219,12 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     like k) to receive the rotated keys, or None when k already holds rotated keys."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v and o must be 4-D [batch, heads, tokens, head_dim]")
-    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+    fp8 = q.dtype in _FP8_DTYPES
+    if fp8:
+        if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != torch.bfloat16:
+            raise ValueError("FP8 attention takes E4M3 q, k, v (uint8 codes or "
+                             "torch.float8_e4m3fn) and a bfloat16 o")
+    elif q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
         raise ValueError("q, k, v and o must share one dtype: float16 or bfloat16")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [batch, heads_q, tokens]")
@@ -228,7 +238,7 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != (b, hq, n):
         raise ValueError("o must match q and lse must be [batch, heads_q, tokens]")
     p = FaFwdParams(
-        dtype=_DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
+        dtype=FA_E4M3 if fp8 else _DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
         o=o.data_ptr(), lse=lse.data_ptr(), batch=b, heads_q=hq, heads_kv=hkv, seqlen=n,
         seqlen_k=nk, head_dim=d, causal=int(bool(causal)), scale=float(scale),
         q_stride=_strides(q), k_stride=_strides(k), v_stride=_strides(v), o_stride=_strides(o))
@@ -276,21 +286,40 @@ def make_params(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tens
     return p
 
 
+def set_descales(p: FaFwdParams, q: torch.Tensor, k: torch.Tensor,
+                 q_descale: Optional[torch.Tensor], k_descale: Optional[torch.Tensor],
+                 v_descale: Optional[torch.Tensor]) -> None:
+    """FP8 descales: contiguous float32 [batch, heads_q] for q, [batch, heads_kv] for k and v."""
+    for name, t, heads in (("q_descale", q_descale, q.shape[1]), ("k_descale", k_descale, k.shape[1]),
+                           ("v_descale", v_descale, k.shape[1])):
+        if t is None:
+            continue
+        if (t.dtype != torch.float32 or tuple(t.shape) != (q.shape[0], heads)
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float32 [batch, heads] tensor on the "
+                             "device of q")
+        setattr(p, name, t.data_ptr())
+
+
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
            lse: torch.Tensor, *, scale: float, causal: bool = False,
            cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
            stream: Optional[torch.cuda.Stream] = None,
            cu_seqlens_k: Optional[torch.Tensor] = None,
            rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
-           rope_interleaved: bool = False, k_rot: Optional[torch.Tensor] = None) -> None:
+           rope_interleaved: bool = False, k_rot: Optional[torch.Tensor] = None,
+           q_descale: Optional[torch.Tensor] = None, k_descale: Optional[torch.Tensor] = None,
+           v_descale: Optional[torch.Tensor] = None) -> None:
     """Enqueues the forward pass writing o and lse, on `stream` (default: torch's current);
-    with RoPE tables also the rotated keys into k_rot (None: k is already rotated)."""
+    with RoPE tables also the rotated keys into k_rot (None: k is already rotated). E4M3 q, k,
+    v (FP8) take per-(batch, head) descales and write a bfloat16 o."""
     lib = load_library()
     for t in (q, k, v, o, lse):
         if not t.is_cuda:
             raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
     p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k,
                     rope_cos, rope_sin, rope_interleaved, k_rot)
+    set_descales(p, q, k, q_descale, k_descale, v_descale)
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         st = int(lib.fa_fwd(ctypes.byref(p), ctypes.c_void_p(s.cuda_stream)))
@@ -404,6 +433,29 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                    rope_cos=rope_cos, rope_sin=rope_sin, rope_interleaved=rope_interleaved,
                    k_rot=k_rot)
     return (o, lse, k_rot) if return_k_rot else (o, lse)
+
+
+def attention_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  q_descale: Optional[torch.Tensor] = None,
+                  k_descale: Optional[torch.Tensor] = None,
+                  v_descale: Optional[torch.Tensor] = None, *, scale: Optional[float] = None,
+                  causal: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
+                  max_seqlen: Optional[int] = None,
+                  cu_seqlens_k: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention on E4M3 q, k, v ([B, H, N, d] codes, uint8 or float8_e4m3fn) standing for
+    codes times their per-(batch, head) descales; returns bfloat16 O and fp32 LSE."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if cu_seqlens is not None and max_seqlen is None:
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+        max_seqlen = int(lens.max()) if lens.numel() else 0
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, cu_seqlens=cu_seqlens,
+           max_seqlen=max_seqlen, cu_seqlens_k=cu_seqlens_k, q_descale=q_descale,
+           k_descale=k_descale, v_descale=v_descale)
+    return o, lse
 
 
 def make_bwd_params(q, k, v, o, dout, lse, dq, dk, dv, delta, scale: float, causal: bool,

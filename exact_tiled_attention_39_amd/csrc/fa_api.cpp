@@ -23,9 +23,9 @@ bool product_exceeds(int64_t a, int64_t b, int64_t c, int64_t limit) {
   return a * b > limit / c;
 }
 
-bool stride_ok(const int64_t s[3], int32_t head_dim, int32_t seqlen) {
+bool stride_ok(const int64_t s[3], int32_t head_dim, int32_t seqlen, int64_t multiple = 8) {
   for (int i = 0; i < 3; ++i)
-    if (s[i] < 0 || (s[i] & 7) != 0) return false;
+    if (s[i] < 0 || s[i] % multiple != 0) return false;
   if (seqlen > 1 && (s[2] < head_dim || s[2] > (int64_t(1) << 23))) return false;
   return true;
 }
@@ -41,9 +41,10 @@ uint32_t fa_params_size(void) { return static_cast<uint32_t>(sizeof(fa_fwd_param
 fa_status fa_check_args(const fa_fwd_params* p) {
   if (p == nullptr) return FA_ERR_NULL;
   if (p->struct_size != sizeof(fa_fwd_params)) return FA_ERR_ABI;
-  if (p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (p->dtype != FA_F16 && p->dtype != FA_BF16 && p->dtype != FA_E4M3) return FA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(p->scale)) return FA_ERR_UNSUPPORTED;
+  if (p->dtype == FA_E4M3 && p->rope_cos != nullptr) return FA_ERR_UNSUPPORTED;
   if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->seqlen < 0 || p->seqlen_k < 0 ||
       p->reserved0 != 0)
     return FA_ERR_SHAPE;
@@ -62,11 +63,15 @@ fa_status fa_check_args(const fa_fwd_params* p) {
   if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
     return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(p->lse) & 3u) != 0) return FA_ERR_ALIGN;
-  if (!stride_ok(p->q_stride, p->head_dim, p->seqlen) ||
-      !stride_ok(p->k_stride, p->head_dim, p->seqlen_k) ||
-      !stride_ok(p->v_stride, p->head_dim, p->seqlen_k) ||
+  const int64_t in_multiple = p->dtype == FA_E4M3 ? 16 : 8;  // 16-byte rows
+  if (!stride_ok(p->q_stride, p->head_dim, p->seqlen, in_multiple) ||
+      !stride_ok(p->k_stride, p->head_dim, p->seqlen_k, in_multiple) ||
+      !stride_ok(p->v_stride, p->head_dim, p->seqlen_k, in_multiple) ||
       !stride_ok(p->o_stride, p->head_dim, p->seqlen))
     return FA_ERR_ALIGN;
+  const float* descales[] = {p->q_descale, p->k_descale, p->v_descale};
+  for (const float* d : descales)
+    if (d != nullptr && (reinterpret_cast<uintptr_t>(d) & 3u) != 0) return FA_ERR_ALIGN;
   if ((p->rope_cos == nullptr) != (p->rope_sin == nullptr)) return FA_ERR_NULL;
   if (p->rope_cos == nullptr) {
     if (p->k_rot != nullptr) return FA_ERR_NULL;
@@ -99,7 +104,8 @@ fa_status fa_fwd(const fa_fwd_params* p, void* stream) {
   if (p->seqlen == 0) return FA_OK;
   if (p->cu_seqlens != nullptr && p->max_seqlen == 0) return FA_OK;
   const char* err = nullptr;
-  const fa_status ls = fa::launch_forward(*p, stream, &err);
+  const fa_status ls = p->dtype == FA_E4M3 ? fa::launch_forward_fp8(*p, stream, &err)
+                                           : fa::launch_forward(*p, stream, &err);
   if (ls != FA_OK && err != nullptr) g_last_hip_error = err;
   return ls;
 }
@@ -110,6 +116,7 @@ namespace {
 fa_status checked_plan(const fa_fwd_params* p, int32_t num_splits, fa::SplitPlan* plan) {
   const fa_status st = fa_check_args(p);
   if (st != FA_OK) return st;
+  if (p->dtype == FA_E4M3) return FA_ERR_UNSUPPORTED;
   if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
   *plan = fa::plan_splitkv(*p, num_splits);
   if (plan->grid > INT32_MAX || (plan->rows_total + 3) / 4 > INT32_MAX) return FA_ERR_SHAPE;
@@ -199,7 +206,8 @@ const char* fa_status_string(int32_t status) {
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
     case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype FA_F16 or FA_BF16, scale finite";
+      return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype FA_F16, FA_BF16 or FA_E4M3, "
+             "scale finite; FA_E4M3 takes no RoPE tables and no split-KV";
     case FA_ERR_ALIGN:
       return "FA_ERR_ALIGN: base pointers must be 16-byte aligned, strides non-negative "
              "multiples of 8 elements, token strides in [head_dim, 2^23]";

@@ -12,6 +12,9 @@ namespace fa {
 // On a HIP error returns FA_ERR_LAUNCH and sets *hip_error to the HIP error text.
 fa_status launch_forward(const fa_fwd_params& p, void* stream, const char** hip_error);
 
+// Enqueues the FP8 (E4M3) forward kernel for arguments that fa_check_args accepted.
+fa_status launch_forward_fp8(const fa_fwd_params& p, void* stream, const char** hip_error);
+
 // Enqueues the RoPE pass that writes the rotated keys to p.k_rot (p.rope_cos set).
 fa_status launch_rope_keys(const fa_fwd_params& p, void* stream, const char** hip_error);
 

@@ -44,19 +44,22 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
   FA_F16 = 0,  /* IEEE binary16 */
-  FA_BF16 = 1  /* bfloat16 */
+  FA_BF16 = 1, /* bfloat16 */
+  FA_E4M3 = 2  /* Q, K, V in OCP FP8 E4M3 with per-(batch, head) descales; O in bfloat16 (see
+                  "FP8" below; fa_fwd only) */
 } fa_dtype;
 
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,       /* a size is out of range, or the grid would not fit */
-  FA_ERR_UNSUPPORTED = 3, /* head_dim not 64 or 128, unknown dtype, or non-finite scale */
+  FA_ERR_UNSUPPORTED = 3, /* head_dim not 64 or 128, unknown dtype, non-finite scale, or
+                             a feature the dtype does not support */
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned, a stride is not a
                              non-negative multiple of 8 elements, or a token stride is below
                              head_dim (overlapping rows) or above 2^23 elements */
@@ -125,6 +128,10 @@ typedef struct fa_fwd_params {
                                   with k_rot_stride; may be k itself with k's strides) and
                                   attention reads them */
   int64_t k_rot_stride[3];
+  /* since ABI version 6: FP8 descales (FA_E4M3 only; NULL means 1 for every head) */
+  const float* q_descale;      /* fp32 [batch, heads_q] */
+  const float* k_descale;      /* fp32 [batch, heads_kv] */
+  const float* v_descale;      /* fp32 [batch, heads_kv] */
 } fa_fwd_params;
 
 /*
@@ -145,6 +152,20 @@ typedef struct fa_fwd_params {
  * rope_rows >= seqlen_k is checked. Errors: FA_ERR_NULL for one table without the other or
  * k_rot without tables; FA_ERR_ALIGN for a table not 16-byte aligned or a bad k_rot layout;
  * FA_ERR_SHAPE for too few table rows. The backward pass takes no RoPE arguments.
+ */
+
+/*
+ * FP8 (dtype FA_E4M3). FP8 matrix cores are FlashAttention-3's second lever (xspy page
+ * "FlashAttention and chunked prefill mechanics", section 1); the pages give no recipe, and
+ * the one here is: Q, K, V hold E4M3 codes (OCP: bias 7, 3 mantissa bits, largest 448, no
+ * infinities), and the tensor a code stands for is its value times the fp32 descale of its
+ * (batch, head). The output is attention on those values: O in bfloat16 (o_stride in bf16
+ * elements), LSE in fp32. S = Q K^T is formed exactly from the codes; the probabilities are
+ * shifted by 2^8 and rounded to E4M3 before the P V product (so |dO| <= max|v| (2^-4 +
+ * keys 2^-18) per row, above bf16 rounding); the log-sum-exp uses unrounded sums. Descales
+ * must be finite (a negative product with scale flips the scores' sign, as a negative scale
+ * does). Q, K, V strides are multiples of 16 elements (16 bytes). Not supported with FA_E4M3:
+ * RoPE tables and fa_fwd_splitkv (FA_ERR_UNSUPPORTED).
  */
 
 /*

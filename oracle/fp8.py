@@ -10,16 +10,22 @@ no recipe. The readings taken here (also listed in the design notes):
     value 448) with one fp32 descale factor per (batch, head): the tensor a code stands for is
     decode(code) * descale. Attention is the definition applied to those decoded values, so
     the oracle is ``attention`` on them.
-  * An FP8 kernel forms S = Q K^T exactly from the codes (fp32 accumulation), applies
+  * An FP8 kernel forms S = Q K^T from the codes on the E4M3 matrix instructions, applies
     scale * descale_q * descale_k to the scores and descale_v to the output, and rounds the
     probabilities to E4M3 before the P V product: P~ = exp2(s - m) is shifted by 2^8 (so the
     largest is 256, inside E4M3's range) and rounded to nearest even. The row sum l uses the
     unrounded values and O is rounded to bf16.
-  * Error bound (``o_tolerance``): rounding P~ to E4M3 changes each weight by at most 2^-4 of
-    itself while it is a normal number, and by at most 2^-10 absolutely (in the shifted units,
-    where l >= 256) once it is subnormal, so |dO| <= max|v| (2^-4 + n_keys 2^-18) per row, plus
-    half a bf16 unit of O. The log-sum-exp comes from the unrounded sum and keeps the forward's
-    1e-5 bound.
+  * Error bounds. The E4M3 matrix instruction of gfx950 (32x32x64) does not add its 64 exact
+    products in full fp32: measured on MI355X over 6 million random products of full-range
+    codes, one instruction's error reached 2^-11.4 of its largest |product| (2^-14 of the sum
+    of |products|), so a score carries an error of at most e_S = |scale| (d / 64) 2^-10
+    max|q| max|k| (``score_error_bound``, 2^-10 leaving a margin of 2.6 over that maximum).
+    The log-sum-exp then errs by at most e_S beyond the forward's 1e-5 relative bound
+    (``lse_tolerance``). Rounding P~ to E4M3 changes each weight by at most 2^-4 of itself while
+    it is a normal number and by at most 2^-10 absolutely (in the shifted units, where
+    l >= 256) once it is subnormal, and the score error moves each weight by a factor within
+    exp(+-2 e_S); so |dO| <= max|v| (2^-4 + n_keys 2^-18 + 2 e_S) per row, plus half a bf16 unit
+    of O (``o_tolerance``).
 """
 from __future__ import annotations
 
@@ -45,7 +51,26 @@ def dequantize(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
     return decode_e4m3(codes) * np.asarray(descale, dtype=np.float64)[:, :, None, None]
 
 
-def o_tolerance(v_values: np.ndarray, n_keys: int) -> float:
+# One 64-term E4M3 MFMA sum errs by at most this fraction of its largest |product| (see above).
+MFMA_E4M3_SUM_ERROR = 2.0 ** -10
+
+
+def score_error_bound(q_values: np.ndarray, k_values: np.ndarray, scale: float,
+                      head_dim: int) -> float:
+    """e_S: the largest score error of an FP8 kernel for these (decoded) Q and K values."""
+    if q_values.size == 0 or k_values.size == 0:
+        return 0.0
+    qmax = float(np.abs(q_values).max())
+    kmax = float(np.abs(k_values).max())
+    return abs(scale) * (head_dim / 64) * MFMA_E4M3_SUM_ERROR * qmax * kmax
+
+
+def lse_tolerance(lse_ref: np.ndarray, score_err: float) -> np.ndarray:
+    """Per-row bound on |LSE_gpu - LSE_ref|: the forward's relative 1e-5 plus e_S."""
+    return 1e-5 * np.maximum(np.abs(lse_ref), 1.0) + score_err
+
+
+def o_tolerance(v_values: np.ndarray, n_keys: int, score_err: float = 0.0) -> float:
     """The bound above for outputs built from these V values (all heads) and n_keys keys."""
     vmax = float(np.abs(v_values).max()) if v_values.size else 0.0
-    return vmax * (2.0 ** -4 + n_keys * 2.0 ** -18) + vmax * 2.0 ** -9
+    return vmax * (2.0 ** -4 + n_keys * 2.0 ** -18 + 2.0 * score_err) + vmax * 2.0 ** -9

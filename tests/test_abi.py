@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_struct_layout():
     assert fa.fa_abi_version() == fa.FA_ABI_VERSION
-    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 264
+    assert fa.fa_params_size() == ctypes.sizeof(fa.FaFwdParams) == 288
     assert fa.FaFwdParams.cu_seqlens.offset == 88
     assert fa.FaFwdParams.o_stride.offset == 168
     assert fa.FaFwdParams.seqlen_k.offset == 192
@@ -47,6 +47,8 @@ def test_abi_version_and_struct_layout():
     assert fa.FaFwdParams.rope_rows.offset == 224
     assert fa.FaFwdParams.k_rot.offset == 232
     assert fa.FaFwdParams.k_rot_stride.offset == 240
+    assert fa.FaFwdParams.q_descale.offset == 264
+    assert fa.FaFwdParams.v_descale.offset == 280
 
 
 ALIGNED = 0x10000
@@ -83,7 +85,7 @@ def test_valid_arguments_pass():
     (dict(q=0), fa.FA_ERR_NULL),
     (dict(lse=0), fa.FA_ERR_NULL),
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=float("inf")), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=float("nan")), fa.FA_ERR_UNSUPPORTED),
     (dict(batch=0), fa.FA_ERR_SHAPE),
@@ -151,6 +153,26 @@ def test_rope_errors_before_any_device_call(kw, status):
     lib = fa.load_library()
     assert lib.fa_fwd(ctypes.byref(p), None) == status
     assert lib.fa_fwd_splitkv(ctypes.byref(p), 1, None, 0, None) == status
+
+
+def test_fp8_arguments():
+    fp8 = dict(dtype=fa.FA_E4M3, q_descale=ALIGNED * 11, k_descale=ALIGNED * 12,
+               v_descale=ALIGNED * 13)
+    assert fa.fa_check_args(good(**fp8)) == fa.FA_OK
+    assert fa.fa_check_args(good(dtype=fa.FA_E4M3)) == fa.FA_OK  # unit descales
+    lib = fa.load_library()
+    bad = [
+        (dict(q_descale=ALIGNED * 11 + 2), fa.FA_ERR_ALIGN),
+        (dict(k_stride=(2 * 100 * 128, 100 * 128, 136)), fa.FA_ERR_ALIGN),  # 136 B rows: not 16 B
+        (dict(**{k: v for k, v in ROPE.items()}), fa.FA_ERR_UNSUPPORTED),  # no RoPE with FP8
+        (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    ]
+    for kw, status in bad:
+        p = good(**{**fp8, **kw})
+        assert fa.fa_check_args(p) == status, kw
+        assert lib.fa_fwd(ctypes.byref(p), None) == status
+    # split-KV has no FP8 path
+    assert lib.fa_fwd_splitkv(ctypes.byref(good(**fp8)), 1, None, 0, None) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_struct_size_mismatch_and_null_params():

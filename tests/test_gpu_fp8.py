@@ -1,0 +1,125 @@
+"""Parity of the FP8 (E4M3) forward (fa_fwd with FA_E4M3, through the C-ABI) with the oracle on
+a gfx950 GPU.
+
+The oracle is the attention definition on the decoded inputs (codes times their descales).
+Tolerances (oracle/fp8.py): the E4M3 matrix instruction sums its 64 products with an error of
+up to 2^-10 of the largest |product|, so scores err by at most e_S = |scale| (d/64) 2^-10
+max|q| max|k|; |dLSE| <= 1e-5 max(|LSE|, 1) + e_S (the row sums are not rounded), and
+|dO| <= max|v| (2^-4 + n_keys 2^-18 + 2 e_S) + half a bf16 unit (the probabilities are rounded
+to E4M3 before the P V product). The mean errors must stay below a sixteenth of those bounds:
+an error that only the worst case allows must stay rare.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8 as ofp8
+import seeded_inputs as si
+from gpu_util import download_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_39_amd as fa
+    fa.load_library()  # fails loudly if the HIP library is missing
+
+
+def _run(inp: si.Inputs8, unit_descales=False):
+    import exact_tiled_attention_39_amd as fa
+
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    ds = (None, None, None) if unit_descales else (up(inp.q_descale), up(inp.k_descale),
+                                                   up(inp.v_descale))
+    cu = up(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+    cu_k = up(inp.cu_seqlens_k) if inp.cu_seqlens_k is not None else None
+    o, lse = fa.attention_fp8(q, k, v, *ds, scale=inp.scale, causal=inp.causal, cu_seqlens=cu,
+                              cu_seqlens_k=cu_k)
+    torch.cuda.synchronize()
+    return si.bits_to_f64(download_bits(o), si.BF16), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(inp: si.Inputs8, what, unit_descales=False):
+    o, lse = _run(inp, unit_descales)
+    ones = lambda d: np.ones_like(d)
+    dq, dk, dv = ((ones(inp.q_descale), ones(inp.k_descale), ones(inp.v_descale))
+                  if unit_descales else (inp.q_descale, inp.k_descale, inp.v_descale))
+    q, k, v = (ofp8.dequantize(inp.q, dq), ofp8.dequantize(inp.k, dk), ofp8.dequantize(inp.v, dv))
+    o_ref, lse_ref = oracle.attention(q, k, v, inp.scale, inp.causal, cu_seqlens=inp.cu_seqlens,
+                                      cu_seqlens_k=inp.cu_seqlens_k)
+    n_keys = inp.k.shape[2]
+    e_s = ofp8.score_error_bound(q, k, inp.scale, inp.q.shape[-1])
+    tol = ofp8.o_tolerance(v, n_keys, e_s)
+    assert np.isfinite(o).all() and not np.isnan(lse).any(), what
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), what
+    err = np.abs(o - o_ref)
+    dl = np.abs(lse[~empty] - lse_ref[~empty])
+    ltol = ofp8.lse_tolerance(lse_ref[~empty], e_s)
+    print(f"{what}: max|dO| {err.max() if err.size else 0:.3e} mean {err.mean() if err.size else 0:.3e}"
+          f" tol {tol:.3e}; |dLSE| max {dl.max() if dl.size else 0:.2e} mean "
+          f"{dl.mean() if dl.size else 0:.2e} e_S {e_s:.2e}", flush=True)
+    if err.size:
+        assert err.max() <= tol, f"{what}: max|dO| {err.max():.3e} > {tol:.3e}"
+        assert err.mean() <= tol / 16, f"{what}: mean|dO| {err.mean():.3e} > {tol / 16:.3e}"
+    if dl.size:
+        assert (dl <= ltol).all(), f"{what}: LSE error {(dl - ltol).max():.3e} above its bound"
+        assert dl.mean() <= ltol.mean() / 16, f"{what}: mean LSE error {dl.mean():.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 129, 257, 520])
+def test_shapes(n, d, causal):
+    inp = si.random_inputs_fp8(2, 4, 2, n, d, seed=800 + n + d, causal=causal)
+    _check(inp, f"fp8 n={n} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 8), (16, 8)])
+def test_grouped_heads(hq, hkv, causal):
+    inp = si.random_inputs_fp8(1, hq, hkv, 300, 128, seed=810 + hq + hkv, causal=causal)
+    _check(inp, f"fp8 gqa {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_sequences(causal):
+    lens_q = (0, 1, 127, 64, 5, 300, 2)
+    lens_k = (3, 1, 300, 64, 0, 300, 700)
+    inp = si.random_inputs_fp8(1, 4, 2, sum(lens_q), 128, seed=820, causal=causal,
+                               seq_lens=lens_q, seqlen_k=sum(lens_k), seq_lens_k=lens_k)
+    _check(inp, "fp8 packed")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(64, 300), (1, 500), (300, 100), (40, 0)])
+def test_query_chunks(nq, nk, causal):
+    inp = si.random_inputs_fp8(2, 4, 4, nq, 64, seed=830 + nq + nk, causal=causal, seqlen_k=nk)
+    _check(inp, f"fp8 chunk {nq}/{nk}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.0])
+def test_scales(scale):
+    inp = si.random_inputs_fp8(1, 4, 4, 200, 128, seed=840, causal=True, scale=scale)
+    _check(inp, f"fp8 scale={scale}")
+
+
+def test_unit_descales():
+    """NULL descale pointers mean 1: the codes are the values."""
+    inp = si.random_inputs_fp8(1, 4, 2, 260, 128, seed=850, causal=True)
+    _check(inp, "fp8 unit descales", unit_descales=True)
+
+
+def test_long_rows_and_determinism():
+    """4096 keys per row (64 tiles of rounded probabilities), and the same bits on a rerun."""
+    inp = si.random_inputs_fp8(1, 2, 2, 4096, 128, seed=860, causal=False)
+    _check(inp, "fp8 n=4096")
+    a, la = _run(inp)
+    b, lb = _run(inp)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)

@@ -41,3 +41,15 @@ def test_tolerance_grows_with_the_values_and_the_key_count():
     v = np.array([0.5, -3.0, 2.0])
     assert ofp8.o_tolerance(v, 0) == 3.0 * (2 ** -4 + 2 ** -9)
     assert ofp8.o_tolerance(v, 2 ** 14) == 3.0 * (2 ** -4 + 2 ** -4 + 2 ** -9)
+
+
+def test_score_and_lse_bounds():
+    q = np.array([[0.5, -2.0]])
+    k = np.array([[3.0, 1.0]])
+    # |scale| * (d / 64) * 2^-10 * max|q| * max|k|
+    assert ofp8.score_error_bound(q, k, -0.25, 128) == 0.25 * 2 * 2 ** -10 * 2.0 * 3.0
+    assert ofp8.score_error_bound(np.zeros((0, 2)), k, 1.0, 64) == 0.0
+    e = 1e-3
+    np.testing.assert_allclose(ofp8.lse_tolerance(np.array([0.5, -20.0]), e),
+                               [1e-5 + e, 20 * 1e-5 + e])
+    assert ofp8.o_tolerance(np.array([2.0]), 0, e) == 2.0 * (2 ** -4 + 2 * e + 2 ** -9)
