@@ -31,7 +31,8 @@ invariants, a library routine, brute force); none is "parity unpinned".
 from .definition import (attention, attention_rows, kv_head, score_matrix_bytes,
                         softmax_rows_with_lse)
 from .online import flash_forward, merge
-from .backward import (attention_backward, attention_backward_dq_rows, output_gradient_rowsum,
+from .backward import (attention_backward, attention_backward_dq_rows,
+                       attention_backward_kv_rows, output_gradient_rowsum,
                        softmax_jacobian_product)
 from . import rope, scalar
 
@@ -47,6 +48,7 @@ __all__ = [
     "rope",
     "attention_backward",
     "attention_backward_dq_rows",
+    "attention_backward_kv_rows",
     "output_gradient_rowsum",
     "softmax_jacobian_product",
 ]

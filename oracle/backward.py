@@ -106,3 +106,41 @@ def attention_backward_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: 
             ds = softmax_jacobian_product(p, doi @ vh[s0:end].T)
             out[r] = scale * (ds @ kh[s0:end])[0]
     return out
+
+
+def attention_backward_kv_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                               scale: float, causal: bool, rows,
+                               chunk: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+    """dK and dV of selected key rows (b, kv_head, token) of a fixed-length self-attention
+    batch: dV_j = sum_i P_ij dO_i and dK_j = scale sum_i dS_ij q_i over every query row i of
+    every query head sharing the kv head. Each query row's softmax (P, its LSE) and D_i need
+    the whole row, so query rows are evaluated exactly, a batch of rows at a time. Returns
+    (dk [R, d], dv [R, d]) in the order of ``rows``."""
+    rows = list(rows)
+    b_, hq, n, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    dk = np.zeros((len(rows), d))
+    dv = np.zeros((len(rows), d))
+    by_head = defaultdict(list)
+    for r, (b, hk, j) in enumerate(rows):
+        by_head[(b, hk)].append(r)
+    for (b, hk), idx in by_head.items():
+        sel = np.array([rows[r][2] for r in idx])
+        kh = np.asarray(k[b, hk], dtype=np.float64)
+        vh = np.asarray(v[b, hk], dtype=np.float64)
+        for h in range(hk * group, (hk + 1) * group):
+            qh = np.asarray(q[b, h], dtype=np.float64)
+            doh = np.asarray(do[b, h], dtype=np.float64)
+            for i0 in range(0, n, chunk):
+                i1 = min(n, i0 + chunk)
+                s = scale * (qh[i0:i1] @ kh.T)
+                allowed = np.ones_like(s, dtype=bool)
+                if causal:
+                    allowed = np.arange(n)[None, :] <= np.arange(i0, i1)[:, None]
+                p, _ = softmax_rows_with_lse(s, allowed)
+                dp = doh[i0:i1] @ vh.T
+                ds = softmax_jacobian_product(p, dp)
+                dv[idx] += p[:, sel].T @ doh[i0:i1]
+                dk[idx] += scale * (ds[:, sel].T @ qh[i0:i1])
+    return dk, dv

@@ -192,3 +192,19 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     else:
         monkeypatch.setattr(ob, attr, fn)
     assert _failures(), f"planted mistake {name} went unnoticed"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_rows_match_full_backward(causal):
+    """Selected dK / dV rows, evaluated row batch by row batch, equal the full backward's."""
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((2, 4, 37, 16))
+    k = rng.standard_normal((2, 2, 37, 16))
+    v = rng.standard_normal((2, 2, 37, 16))
+    do = rng.standard_normal((2, 4, 37, 16))
+    _, dk, dv = oracle.attention_backward(q, k, v, do, 0.3, causal)
+    rows = [(0, 0, 0), (0, 1, 36), (1, 0, 17), (1, 1, 5), (1, 1, 6)]
+    dk_r, dv_r = oracle.attention_backward_kv_rows(q, k, v, do, 0.3, causal, rows, chunk=10)
+    for r, (b, hk, j) in enumerate(rows):
+        np.testing.assert_allclose(dk_r[r], dk[b, hk, j], atol=1e-12)
+        np.testing.assert_allclose(dv_r[r], dv[b, hk, j], atol=1e-12)
