@@ -16,9 +16,16 @@
 //    must carry V[key(h, j)][m] in byte j: it comes from four ds_read_b64_tr_b8 per MFMA over
 //    512-byte blocks laid out so that every direct-to-LDS lane still fetches 16 contiguous
 //    bytes of one V row (see TrBlock below).
-//  * Probabilities are rounded to E4M3 before the P V product. E4M3 tops out at 448, so the
-//    running maximum is exact per tile (not raised lazily) and the exponent is shifted by 8:
-//    P~ = 2^(s c - m + 8) <= 256. The row sum keeps the unrounded values.
+//  * Probabilities are rounded to E4M3 before the P V product. The running maximum is raised
+//    lazily, as in the 16-bit kernel (the exact tile maximum, a serial reduction and a
+//    cross-lane exchange ahead of every exponential, measured 18 % of the kernel's time), so a
+//    probability may exceed E4M3's 448. The MFMA's E8M0 block scales take care of that: the
+//    64 keys of a tile form two scale blocks of 32 (key half kb, both lane halves of a query
+//    column), each scaled by its own power of two, lane n giving block 0's and lane n + 32
+//    block 1's. Each block is divided by 2^k before rounding, k = max(0, e - 7) for a block sum
+//    in [2^e, 2^(e+1)), so no value exceeds 2^8, and the MFMA multiplies 2^k back exactly.
+//    Exponentials carry a shift of 8 (2^(s c - m + 8)) so that small probabilities keep
+//    E4M3's normal range. The row sum keeps the unrounded values.
 //  * Scores are scaled by c = |scale * descale_q * descale_k| log2(e) (a negative product
 //    negates Q's sign bits), and O is multiplied by descale_v / l and stored as bf16.
 #include <hip/hip_runtime.h>
@@ -38,6 +45,7 @@ using namespace dev;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockM = 256;
 constexpr int kBlockN = 64;
@@ -82,6 +90,32 @@ struct Geo8 {
   static_assert(kKBlocks == kVBlocks, "K and V tiles have the same size");
 };
 
+// Sum and maximum of a value over lanes L and L ^ 32 with v_permlane32_swap (a VALU exchange;
+// __shfl_xor goes through the LDS permute unit and its latency). The instruction swaps lanes
+// 32..63 of its first operand with lanes 0..31 of its second, so swapping x with a copy of
+// itself leaves lanes 0..31's values in the first register and lanes 32..63's in the second,
+// in every lane. It is written as inline assembly with both registers as read-write operands:
+// the compiler builtin's second result was folded into the first (r[0] + r[1] became 2 r[0]).
+// The s_nop pairs give the wait states around a permlane that the compiler would otherwise
+// insert itself.
+__device__ __forceinline__ void halves_of(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x);
+  uint32_t b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves_of(x, lo, hi);
+  return lo + hi;
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves_of(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+
 // The key carried in byte j (0..31) of a P^T / V^T operand lane of half h.
 __host__ __device__ constexpr int key_of_byte(int h, int j) {
   return 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h + (j & 3);
@@ -117,6 +151,16 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   // E4M3 x E4M3 (format 0 for both operands), unit block scales (E8M0 127 = 2^0)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+// The same with a per-lane E8M0 scale for the B operand: bytes 0..15 of lanes n and n + 32 (K
+// block 0) take lane n's scale, bytes 16..31 of both (K block 1) lane n + 32's.
+__device__ __forceinline__ f32x16 mfma8_bscaled(i32x8 a, i32x8 b, f32x16 c, int b_scale) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, b_scale);
+}
+
+// A tile is rescaled (its maximum formed) only when some lane's sum of shifted exponentials
+// exceeds this (2^15 relative to the reference maximum, times the shift 2^8).
+constexpr float kLazyBound8 = 8388608.0f;
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
@@ -269,6 +313,7 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
   for (int j = 0; j < kOBlocks; ++j) oacc[j] = f32x16{};
   f32x16 sacc[2];
   i32x8 pb = i32x8{0, 0, 0, 0, 0, 0, 0, 0};  // P^T of the previous tile, E4M3
+  int pscale = 127;                           // its E8M0 block scale (this lane's block)
 
   // M phase: the 2 kSteps S MFMAs of tile p (K stage KS) and the kOBlocks P V MFMAs of tile
   // p - 1 (V stage VS), alternating in pairs, each operand read kAhead MFMAs ahead.
@@ -314,7 +359,7 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
         sacc[kb] = mfma8(opnd[n], qf[s], s == 0 ? f32x16{} : sacc[kb]);
       } else {
         constexpr int jb = pv_idx(n);
-        oacc[jb] = mfma8(opnd[n], pb, oacc[jb]);
+        oacc[jb] = mfma8_bscaled(opnd[n], pb, oacc[jb], pscale);
       }
     };
     [&]<int... n>(std::integer_sequence<int, n...>) {
@@ -331,7 +376,8 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
     }(std::make_integer_sequence<int, kMfma>{});
   };
 
-  // Online softmax of a tile (Theorem 2) with the exact tile maximum; P rounded to E4M3.
+  // Online softmax of a tile (Theorem 2) with a lazily raised reference maximum; P rounded to
+  // E4M3 under per-block power-of-two scales.
   auto softmax = [&](int tile) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     const int key0 = tile * kBlockN;
@@ -346,41 +392,62 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
           sacc[kb][i] = off <= lim ? sacc[kb][i] : -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    float ex[2][16];
+    float part[2][2];  // per key half, two interleaved partial sums
+    auto expo = [&]() __attribute__((always_inline)) {
+      const float off = 8.f - m_run;  // shifted by 2^8; +inf before the first tile
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    const float m_tile = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run)) {
-      const float m_new = fmaxf(m_run, m_tile);
+        for (int i = 0; i < 16; ++i) {
+          ex[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, off));
+          if (i < 2)
+            part[kb][i] = ex[kb][i];
+          else
+            part[kb][i & 1] += ex[kb][i];
+        }
+    };
+    expo();
+    float s0 = part[0][0] + part[0][1];
+    float s1 = part[1][0] + part[1][1];
+    // Rare path: the first tile (no reference yet), or a score far above the reference; NaN
+    // sums land here too and propagate either way.
+    if (__builtin_amdgcn_ballot_w64(!(s0 + s1 <= kLazyBound8))) {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      const float m_new = fmaxf(m_run, max_halves(mx) * c);
       const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
+      if (m_run == -INFINITY) m_run = 0.f;  // nothing visible yet: any reference will do
+      expo();
+      s0 = part[0][0] + part[0][1];
+      s1 = part[1][0] + part[1][1];
     }
-    const float off = 8.f - (m_run == -INFINITY ? 0.f : m_run);  // P~ <= 2^8
-    float ex[2][16];
-    float part[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ex[kb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, off));
-        if (kb == 0 && i < 4)
-          part[i] = ex[kb][i];
-        else
-          part[i & 3] += ex[kb][i];
-      }
-    l_run += (part[0] + part[1]) + (part[2] + part[3]);
-    // byte j of P^T is entry j % 16 of key half j / 16
+    l_run += s0 + s1;
+    // block sums over both lane halves of this query column; 2^k with k = max(0, e - 7)
+    const float b0 = sum_halves(s0);
+    const float b1 = sum_halves(s1);
+    const int k0 = max(int((__builtin_bit_cast(uint32_t, b0) >> 23) & 0xFF) - 127 - 7, 0);
+    const int k1 = max(int((__builtin_bit_cast(uint32_t, b1) >> 23) & 0xFF) - 127 - 7, 0);
+    const float d0 = __builtin_bit_cast(float, uint32_t(127 + k0) << 23);  // 2^k0
+    const float d1 = __builtin_bit_cast(float, uint32_t(127 + k1) << 23);
+    pscale = 127 + (half ? k1 : k0);
+    // byte j of P^T is entry j % 16 of key half j / 16; v_cvt_scalef32_pk_fp8_f32 rounds
+    // value / 2^k to E4M3 (nearest even) in one instruction per pair
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, i = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(ex[kb][i], ex[kb][i + 1], 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(ex[kb][i + 2], ex[kb][i + 3], x, true);
-      pb[w] = x;
+      const float d = kb ? d1 : d0;
+      v2s x = v2s{0, 0};
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, ex[kb][i], ex[kb][i + 1], d, false);
+      x = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(x, ex[kb][i + 2], ex[kb][i + 3], d, true);
+      pb[w] = __builtin_bit_cast(int, x);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -447,7 +514,7 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
 
   // ---- epilogue: O = dv O~ / l (bf16), LSE = (m + log2 l - 8) ln 2 ----------------------
   if (wrow0 >= slen || wrow0 + 32 <= 0) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (qrow >= 0 && qrow < slen) {
     const bool empty = (CAUSAL ? min(klen, qrow + shift + 1) : klen) <= 0;
     const float inv = empty ? 0.f : dv / l_tot;

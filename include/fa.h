@@ -160,9 +160,12 @@ typedef struct fa_fwd_params {
  * the one here is: Q, K, V hold E4M3 codes (OCP: bias 7, 3 mantissa bits, largest 448, no
  * infinities), and the tensor a code stands for is its value times the fp32 descale of its
  * (batch, head). The output is attention on those values: O in bfloat16 (o_stride in bf16
- * elements), LSE in fp32. S = Q K^T is formed exactly from the codes; the probabilities are
- * shifted by 2^8 and rounded to E4M3 before the P V product (so |dO| <= max|v| (2^-4 +
- * keys 2^-18) per row, above bf16 rounding); the log-sum-exp uses unrounded sums. Descales
+ * elements), LSE in fp32. S = Q K^T is formed on the E4M3 matrix instructions, whose own sum
+ * of 64 products errs by up to about 2^-11 of the largest product (measured); the
+ * probabilities are shifted by 2^8, scaled per block of 32 keys by a power of two (the
+ * instruction's E8M0 block scale undoes it) and rounded to E4M3 before the P V product, so
+ * |dO| <= max|v| (2^-4 + keys 2^-18 + 2^-12) per row beyond the score error and bf16
+ * rounding; the log-sum-exp uses unrounded sums. Descales
  * must be finite (a negative product with scale flips the scores' sign, as a negative scale
  * does). Q, K, V strides are multiples of 16 elements (16 bytes). Not supported with FA_E4M3:
  * RoPE tables and fa_fwd_splitkv (FA_ERR_UNSUPPORTED).

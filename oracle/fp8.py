@@ -12,20 +12,24 @@ no recipe. The readings taken here (also listed in the design notes):
     the oracle is ``attention`` on them.
   * An FP8 kernel forms S = Q K^T from the codes on the E4M3 matrix instructions, applies
     scale * descale_q * descale_k to the scores and descale_v to the output, and rounds the
-    probabilities to E4M3 before the P V product: P~ = exp2(s - m) is shifted by 2^8 (so the
-    largest is 256, inside E4M3's range) and rounded to nearest even. The row sum l uses the
-    unrounded values and O is rounded to bf16.
+    probabilities to E4M3 before the P V product: P~ = exp2(s - m) shifted by 2^8 against a
+    reference maximum m, then, for each block of 32 keys of a query row, divided by a power of
+    two 2^k chosen from the block's sum B (k = max(0, e - 7) for B in [2^e, 2^(e+1)), so every
+    value stays below 2^8, inside E4M3's range) and rounded to nearest even; the matrix
+    instruction's block scale multiplies 2^k back exactly. The row sum l uses the unrounded
+    values (l >= 2^8) and O is rounded to bf16.
   * Error bounds. The E4M3 matrix instruction of gfx950 (32x32x64) does not add its 64 exact
     products in full fp32: measured on MI355X over 6 million random products of full-range
     codes, one instruction's error reached 2^-11.4 of its largest |product| (2^-14 of the sum
     of |products|), so a score carries an error of at most e_S = |scale| (d / 64) 2^-10
     max|q| max|k| (``score_error_bound``, 2^-10 leaving a margin of 2.6 over that maximum).
     The log-sum-exp then errs by at most e_S beyond the forward's 1e-5 relative bound
-    (``lse_tolerance``). Rounding P~ to E4M3 changes each weight by at most 2^-4 of itself while
-    it is a normal number and by at most 2^-10 absolutely (in the shifted units, where
-    l >= 256) once it is subnormal, and the score error moves each weight by a factor within
-    exp(+-2 e_S); so |dO| <= max|v| (2^-4 + n_keys 2^-18 + 2 e_S) per row, plus half a bf16 unit
-    of O (``o_tolerance``).
+    (``lse_tolerance``). Rounding to E4M3 changes each weight by at most 2^-4 of itself while it
+    is a normal number, and by at most 2^(k-10) <= max(2^-10, B 2^-17) once it is subnormal, so
+    a block of 32 errs by at most max(2^-5, B 2^-12) absolutely; over the n_keys / 32 blocks of
+    a row, relative to l >= 2^8, that is at most n_keys 2^-18 + 2^-12. The score error moves
+    each weight by a factor within exp(+-2 e_S). So |dO| <= max|v| (2^-4 + n_keys 2^-18 +
+    2^-12 + 2 e_S) per row, plus half a bf16 unit of O (``o_tolerance``).
 """
 from __future__ import annotations
 
@@ -73,4 +77,4 @@ def lse_tolerance(lse_ref: np.ndarray, score_err: float) -> np.ndarray:
 def o_tolerance(v_values: np.ndarray, n_keys: int, score_err: float = 0.0) -> float:
     """The bound above for outputs built from these V values (all heads) and n_keys keys."""
     vmax = float(np.abs(v_values).max()) if v_values.size else 0.0
-    return vmax * (2.0 ** -4 + n_keys * 2.0 ** -18 + 2.0 * score_err) + vmax * 2.0 ** -9
+    return vmax * (2.0 ** -4 + n_keys * 2.0 ** -18 + 2.0 ** -12 + 2.0 * score_err) + vmax * 2.0 ** -9

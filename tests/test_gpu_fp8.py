@@ -5,7 +5,7 @@ The oracle is the attention definition on the decoded inputs (codes times their 
 Tolerances (oracle/fp8.py): the E4M3 matrix instruction sums its 64 products with an error of
 up to 2^-10 of the largest |product|, so scores err by at most e_S = |scale| (d/64) 2^-10
 max|q| max|k|; |dLSE| <= 1e-5 max(|LSE|, 1) + e_S (the row sums are not rounded), and
-|dO| <= max|v| (2^-4 + n_keys 2^-18 + 2 e_S) + half a bf16 unit (the probabilities are rounded
+|dO| <= max|v| (2^-4 + n_keys 2^-18 + 2^-12 + 2 e_S) + half a bf16 unit (the probabilities are rounded
 to E4M3 before the P V product). The mean errors must stay below a sixteenth of those bounds:
 an error that only the worst case allows must stay rare.
 """

@@ -39,8 +39,8 @@ def test_dequantize_applies_one_factor_per_batch_and_head():
 
 def test_tolerance_grows_with_the_values_and_the_key_count():
     v = np.array([0.5, -3.0, 2.0])
-    assert ofp8.o_tolerance(v, 0) == 3.0 * (2 ** -4 + 2 ** -9)
-    assert ofp8.o_tolerance(v, 2 ** 14) == 3.0 * (2 ** -4 + 2 ** -4 + 2 ** -9)
+    assert ofp8.o_tolerance(v, 0) == 3.0 * (2 ** -4 + 2 ** -12) + 3.0 * 2 ** -9
+    assert ofp8.o_tolerance(v, 2 ** 14) == 3.0 * (2 ** -4 + 2 ** -4 + 2 ** -12) + 3.0 * 2 ** -9
 
 
 def test_score_and_lse_bounds():
@@ -52,4 +52,4 @@ def test_score_and_lse_bounds():
     e = 1e-3
     np.testing.assert_allclose(ofp8.lse_tolerance(np.array([0.5, -20.0]), e),
                                [1e-5 + e, 20 * 1e-5 + e])
-    assert ofp8.o_tolerance(np.array([2.0]), 0, e) == 2.0 * (2 ** -4 + 2 * e + 2 ** -9)
+    assert ofp8.o_tolerance(np.array([2.0]), 0, e) == 2.0 * (2 ** -4 + 2 ** -12 + 2 * e) + 2.0 * 2 ** -9
