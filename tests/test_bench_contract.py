@@ -1,0 +1,64 @@
+"""The bench's one-line JSON contract: every key a bench line must carry, their types and the
+relations between them, and the refusal of more than one GPU (the library measures one)."""
+from __future__ import annotations
+
+import json
+import pathlib
+import subprocess
+import sys
+
+import pytest
+
+import seeded_inputs as si
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+BENCH = str(ROOT / "bench.py")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert not r.stdout.strip()
+
+
+@pytest.mark.gpu
+def test_headline_bench_line_carries_the_contract():
+    print("bench.py --steps 3 --warmup 1 --cpu-seconds 1 (headline workload)", flush=True)
+    r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "1",
+                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=600,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-3000:]
+    line = json.loads(lines[0])
+
+    for key, typ in [("metric", str), ("value", float), ("unit", str), ("n_gpus", int),
+                     ("steps", int), ("warmup", int), ("ms_per_step", float),
+                     ("higher_is_better", bool), ("scaling", str), ("dtype", str),
+                     ("data", str), ("config", dict), ("roofline", dict),
+                     ("cpu_baseline", dict)]:
+        assert isinstance(line[key], typ), key
+    assert "vs_baseline" in line and line["vs_baseline"] is None
+    assert line["unit"] == "TFLOP/s" and line["higher_is_better"] is True
+    assert (line["n_gpus"], line["steps"], line["warmup"]) == (1, 3, 1)
+    assert line["scaling"] == "weak" and line["dtype"] == si.BF16
+    assert line["config"]["workload"] == si.HEADLINE
+    # value is the workload's FLOPs over the wall time of one step
+    flop = line["config"]["flop_count"]
+    assert flop == 32 * 4 * 16384 ** 2 * 128 / 2
+    assert line["value"] == pytest.approx(flop / (line["ms_per_step"] * 1e-3) / 1e12, rel=2e-3)
+
+    roof = line["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert 0.0 < roof["achieved"] < roof["peak"]
+    assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-3)
+    assert roof["traffic"] is None or roof["traffic"] > 0
+
+    cpu = line["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s"
+    assert cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+
+    par = line["parity"]
+    assert par["max_abs_dO"] <= 1.6e-2 and par["max_lse_err"] <= 1e-5
