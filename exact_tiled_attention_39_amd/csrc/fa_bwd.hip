@@ -224,9 +224,12 @@ __device__ __forceinline__ void tile_sync() {
 // dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
 // each, waves 4-7 dK for the same keys; a SIMD holds one of each. Per tile, in two phases
 // separated by a barrier: the dV wave forms S = Q K^T and P (masked), and hands P (fp32) to its
-// dK partner through LDS, while the dK wave forms dP = dO V^T; then the dV wave accumulates
-// dV^T += dO^T P while the dK wave forms dS = P (dP - D) and accumulates dK^T += Q^T dS. Each
-// wave does 16 of the tile's 32 products and keeps its state within 256 registers.
+// dK partner through LDS, while the dK wave forms dP = dO V^T and then accumulates
+// dK^T += Q^T dS of the previous tile; then the dV wave accumulates dV^T += dO^T P while the dK
+// wave forms dS = P (dP - D). The dK update thus runs beside the dV wave's exponentials instead
+// of beside its matrix products, and the tiles move through a three-stage LDS ring (the
+// previous tile's Q^T is still read while the next tile lands). Each wave does 16 of the
+// tile's 32 products and keeps its state within 256 registers.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -241,8 +244,9 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   constexpr int kQop = 0, kDop = G::kTileBytes, kQtr = 2 * G::kTileBytes,
                 kDtr = 3 * G::kTileBytes, kLse = 4 * G::kTileBytes, kDel = kLse + 1024;
   constexpr int kStage = kLse + 2048;
-  constexpr int kPbuf = 2 * kStage;  // P of each key group: 4 x (16 fp32 per lane)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage + 4 * 4096];
+  constexpr int kRing = 3;           // tile stages
+  constexpr int kPbuf = kRing * kStage;  // P of each key group: 4 x (16 fp32 per lane)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage + 4 * 4096];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -330,12 +334,18 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     f32x16 part;   // S (dV role) or dP (dK role) of the current tile
     u32x4 pb[2];   // P (dV role) packed as the B operand of the row contraction
 
-    // phase 1: S and P (dV role, P also stored for the partner) or dP (dK role)
+    // phase 1: S and P (dV role, P also stored for the partner) or dP and the previous tile's
+    // dK^T += Q^T dS (dK role)
     auto phase1 = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
       part = chain_over_d<BF16, kSteps>(sb + (DK ? kDop : kQop) + lane * 16, rf);
-      if constexpr (!DK) {
+      if constexpr (DK) {
+        if (st > 0)
+          chain_over_rows<BF16, kOBlocks>(smem + ((ST + kRing - 1) % kRing) * kStage + kQtr +
+                                              lane * 8,
+                                          pb, acc);
+      } else {
         const int r0 = (t_first + st % per_head) * kTileRows;
         // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
         float lse[16], pv[16];
@@ -362,7 +372,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
             pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
       }
     };
-    // phase 2: dV^T += dO^T P (dV role) or dS = P (dP - D), dK^T += Q^T dS (dK role)
+    // phase 2: dV^T += dO^T P (dV role) or dS = P (dP - D) (dK role; its product with Q^T
+    // runs in the next tile's phase 1)
     auto phase2 = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
@@ -381,12 +392,15 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
+      } else {
+        chain_over_rows<BF16, kOBlocks>(sb + kDtr + lane * 8, pb, acc);
       }
-      chain_over_rows<BF16, kOBlocks>(sb + (DK ? kQtr : kDtr) + lane * 8, pb, acc);
     };
     auto step = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
-      if (st + 1 < n_steps) issue(Int<1 - ST>{}, st + 1);
+      // the stage of tile st + 1 last held tile st - 2, whose reads ended before the barrier
+      // that closed step st - 1
+      if (st + 1 < n_steps) issue(Int<(ST + 1) % kRing>{}, st + 1);
       phase1(Int<ST>{}, st);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P is in LDS
       __syncthreads();
@@ -397,10 +411,16 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     if (n_steps > 0) {
       issue(Int<0>{}, 0);
       tile_sync();
-      for (int st = 0; st < n_steps; st += 2) {
+      for (int st = 0; st < n_steps; st += kRing) {
         step(Int<0>{}, st);
         if (st + 1 < n_steps) step(Int<1>{}, st + 1);
+        if (st + 2 < n_steps) step(Int<2>{}, st + 2);
       }
+      // the last tile's dK^T += Q^T dS (its stage is not overwritten: no tile follows)
+      if constexpr (DK)
+        chain_over_rows<BF16, kOBlocks>(smem + ((n_steps - 1) % kRing) * kStage + kQtr +
+                                            lane * 8,
+                                        pb, acc);
     }
     if (key < slen) {
       if constexpr (DK)
