@@ -222,14 +222,14 @@ __device__ __forceinline__ void tile_sync() {
 
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
-// each, waves 4-7 dK for the same keys; a SIMD holds one of each. Per tile, in two phases
-// separated by a barrier: the dV wave forms S = Q K^T and P (masked), and hands P (fp32) to its
-// dK partner through LDS, while the dK wave forms dP = dO V^T and then accumulates
-// dK^T += Q^T dS of the previous tile; then the dV wave accumulates dV^T += dO^T P while the dK
-// wave forms dS = P (dP - D). The dK update thus runs beside the dV wave's exponentials instead
-// of beside its matrix products, and the tiles move through a three-stage LDS ring (the
-// previous tile's Q^T is still read while the next tile lands). Each wave does 16 of the
-// tile's 32 products and keeps its state within 256 registers.
+// each, waves 4-7 dK for the same keys; a SIMD holds one of each. The dK wave runs one tile
+// behind the dV wave, so that each wave's whole tile needs one barrier: in step t the dV wave
+// forms S = Q K^T and P (masked) of tile t, hands P (fp32) to its dK partner through a
+// double-buffered LDS slot and accumulates dV^T += dO^T P; the dK wave forms dP = dO V^T of
+// tile t - 1, dS = P (dP - D) from the P handed over in step t - 1, and accumulates
+// dK^T += Q^T dS. Tiles move through a three-stage LDS ring (tiles t - 1, t and t + 1 in
+// flight). Each wave does 16 of a tile's 32 products and keeps its state within 256
+// registers; the two waves of a SIMD interleave their matrix and element-wise work freely.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -245,8 +245,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
                 kDtr = 3 * G::kTileBytes, kLse = 4 * G::kTileBytes, kDel = kLse + 1024;
   constexpr int kStage = kLse + 2048;
   constexpr int kRing = 3;           // tile stages
-  constexpr int kPbuf = kRing * kStage;  // P of each key group: 4 x (16 fp32 per lane)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage + 4 * 4096];
+  constexpr int kPbuf = kRing * kStage;  // P of each key group, two slots of 4 x 16 fp32/lane
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage + 2 * 4 * 4096];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -311,8 +311,9 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     }
   };
 
-  // P hand-off: entries 4 g .. 4 g + 3 of lane L at 1 KB block g, byte 16 L
+  // P hand-off, slot t % 2: entries 4 g .. 4 g + 3 of lane L at 1 KB block g, byte 16 L
   unsigned char* pbuf = smem + kPbuf + (wave & 3) * 4096 + lane * 16;
+  constexpr int kPslot = 4 * 4096;
 
   // one role's loop; both roles run the same barriers
   auto run = [&](auto role_c) __attribute__((always_inline)) {
@@ -334,77 +335,74 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     f32x16 part;   // S (dV role) or dP (dK role) of the current tile
     u32x4 pb[2];   // P (dV role) packed as the B operand of the row contraction
 
-    // phase 1: S and P (dV role, P also stored for the partner) or dP and the previous tile's
-    // dK^T += Q^T dS (dK role)
-    auto phase1 = [&](auto stage, int st) __attribute__((always_inline)) {
+    // dV role, tile st in stage ST: S, P (masked; stored for the partner in slot st % 2),
+    // dV^T += dO^T P
+    auto dv_tile = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
-      part = chain_over_d<BF16, kSteps>(sb + (DK ? kDop : kQop) + lane * 16, rf);
-      if constexpr (DK) {
-        if (st > 0)
-          chain_over_rows<BF16, kOBlocks>(smem + ((ST + kRing - 1) % kRing) * kStage + kQtr +
-                                              lane * 8,
-                                          pb, acc);
-      } else {
-        const int r0 = (t_first + st % per_head) * kTileRows;
-        // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
-        float lse[16], pv[16];
-        read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
-        const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
+      part = chain_over_d<BF16, kSteps>(sb + kQop + lane * 16, rf);
+      const int r0 = (t_first + st % per_head) * kTileRows;
+      // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
+      float lse[16], pv[16];
+      read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
+      const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = fmaf(part[i], p.c, lse[i] * -kLog2e);
-          if (edge) {
-            const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
-            x = ok ? x : -INFINITY;
-          }
-          pv[i] = __builtin_amdgcn_exp2f(x);
+      for (int i = 0; i < 16; ++i) {
+        float x = fmaf(part[i], p.c, lse[i] * -kLog2e);
+        if (edge) {
+          const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
+          x = ok ? x : -INFINITY;
         }
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<f32x4*>(pbuf + g * 1024) =
-              f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
+        pv[i] = __builtin_amdgcn_exp2f(x);
       }
+      unsigned char* slot = pbuf + (st & 1) * kPslot;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(slot + g * 1024) =
+            f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
+      chain_over_rows<BF16, kOBlocks>(sb + kDtr + lane * 8, pb, acc);
     };
-    // phase 2: dV^T += dO^T P (dV role) or dS = P (dP - D) (dK role; its product with Q^T
-    // runs in the next tile's phase 1)
-    auto phase2 = [&](auto stage, int st) __attribute__((always_inline)) {
+    // dK role, tile st in stage ST (one step behind the dV wave): dP, dS = P (dP - D) with the
+    // P of slot st % 2, dK^T += Q^T dS
+    auto dk_tile = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
-      if constexpr (DK) {
-        float del[16];
-        read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
-        float ds[16];
+      part = chain_over_d<BF16, kSteps>(sb + kDop + lane * 16, rf);
+      float del[16];
+      read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
+      const unsigned char* slot = pbuf + (st & 1) * kPslot;
+      float ds[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 pv = *reinterpret_cast<const f32x4*>(pbuf + g * 1024);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(slot + g * 1024);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (part[4 * g + r] - del[4 * g + r]);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
-      } else {
-        chain_over_rows<BF16, kOBlocks>(sb + kDtr + lane * 8, pb, acc);
+        for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (part[4 * g + r] - del[4 * g + r]);
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
+      chain_over_rows<BF16, kOBlocks>(sb + kQtr + lane * 8, pb, acc);
     };
+    // Step st: issue tile st + 1 (its stage last held tile st - 2, whose last reader, the dK
+    // wave in step st - 1, finished before that step's closing barrier); the dV wave runs tile
+    // st, the dK wave tile st - 1 (P of tile st - 1 was stored before the same barrier); the
+    // closing barrier also waits for tile st + 1.
     auto step = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
-      // the stage of tile st + 1 last held tile st - 2, whose reads ended before the barrier
-      // that closed step st - 1
       if (st + 1 < n_steps) issue(Int<(ST + 1) % kRing>{}, st + 1);
-      phase1(Int<ST>{}, st);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): P is in LDS
-      __syncthreads();
-      phase2(Int<ST>{}, st);
+      if constexpr (DK) {
+        if (st > 0) dk_tile(Int<(ST + kRing - 1) % kRing>{}, st - 1);
+      } else {
+        dv_tile(Int<ST>{}, st);
+      }
       tile_sync();
     };
 
@@ -416,11 +414,16 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
         if (st + 1 < n_steps) step(Int<1>{}, st + 1);
         if (st + 2 < n_steps) step(Int<2>{}, st + 2);
       }
-      // the last tile's dK^T += Q^T dS (its stage is not overwritten: no tile follows)
-      if constexpr (DK)
-        chain_over_rows<BF16, kOBlocks>(smem + ((n_steps - 1) % kRing) * kStage + kQtr +
-                                            lane * 8,
-                                        pb, acc);
+      // the dK wave's last tile (its stage and P slot are not overwritten: no tile follows)
+      if constexpr (DK) {
+        const int last = n_steps - 1;
+        if (last % kRing == 0)
+          dk_tile(Int<0>{}, last);
+        else if (last % kRing == 1)
+          dk_tile(Int<1>{}, last);
+        else
+          dk_tile(Int<2>{}, last);
+      }
     }
     if (key < slen) {
       if constexpr (DK)
