@@ -11,15 +11,16 @@
 // Three launches on the caller's stream:
 //  * fa_bwd_delta_kernel: D = rowsum(dO * O) in fp32 (into the caller's delta buffer).
 //  * fa_bwd_dkdv_kernel: one workgroup per 128 keys of a (batch entry or sequence, kv head).
-//    Its 4 waves own 32 keys each, with K and V resident in registers as MFMA B operands and
-//    dK^T, dV^T accumulating in fp32. 64-query tiles of Q and dO (of every query head that
-//    shares the kv head) stream through double-buffered LDS. Per tile and wave:
-//    S = Q K^T and dP = dO V^T (lane = key, as B operand), P and dS in registers, then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposing LDS reads.
-//  * fa_bwd_dq_kernel: one workgroup per 128 queries of a (batch entry or sequence, query
-//    head). Its 4 waves own 32 queries each, with Q^T and dO^T resident, and dQ^T
-//    accumulating. 64-key tiles of K and V stream through LDS. Per tile and wave:
-//    S^T = K Q^T and dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T.
+//    Each SIMD runs a dV wave and a dK wave for the same 32 keys, with K (dV wave) or V (dK
+//    wave) resident in registers as MFMA B operands and dV^T or dK^T accumulating in fp32.
+//    32-query tiles of Q and dO (of every query head that shares the kv head) stream through a
+//    three-stage LDS ring. The dV wave forms S = Q K^T and P of a tile, hands P to the dK wave
+//    through LDS and accumulates dV^T += dO^T P; the dK wave, one tile behind, forms
+//    dP = dO V^T, dS = P (dP - D) and accumulates dK^T += Q^T dS.
+//  * fa_bwd_dq_kernel: one workgroup per 256 queries of a (batch entry or sequence, query
+//    head). Its 8 waves own 32 queries each, with Q^T and dO^T resident, and dQ^T
+//    accumulating. 32-key tiles of K and V stream through double-buffered LDS. Per tile and
+//    wave: S^T = K Q^T and dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV recomputes S and dP once more, but every gradient accumulates in
 // one workgroup's registers: no atomics, and the result is deterministic.
 // All MFMAs are v_mfma_f32_32x32x16_{bf16,f16}; P and dS are rounded to the input type (round
@@ -177,7 +178,7 @@ __device__ __forceinline__ void load_resident(const uint16_t* base, int64_t sn, 
 // ---------------------------------------------------------------------------------------
 // Both main kernels run 8 waves, two per SIMD, each wave within 256 registers, so that the
 // SIMD interleaves one wave's element-wise work with the other's matrix products. A tile of 32
-// rows of the streamed side moves through double-buffered LDS per step.
+// rows of the streamed side moves through LDS per step (three stages for dK/dV, two for dQ).
 
 constexpr int kWaves = 8;
 constexpr int kThreads8 = 64 * kWaves;
