@@ -162,6 +162,12 @@ def time_calls(torch, step, warmup: int, steps: int):
     return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
 
 
+def launch_percentiles(ms) -> list:
+    """p10, median and p90 of the per-launch durations (ms), the spread of the timed launches."""
+    q = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return [round(float(x), 4) for x in q]
+
+
 def rope_tables(positions: int, head_dim: int, base: float = 10000.0):
     """Standard RoPE tables, fp32 [positions, head_dim / 2]: cos and sin of p * base^(-2i/d)."""
     inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
@@ -296,6 +302,7 @@ def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
         "kernel": "fa_fwd_kernel",
         "avg_launch_ms": round(avg_kernel_ms, 4),
         "launch_ms_min_max": [round(min(kernel_ms), 4), round(max(kernel_ms), 4)],
+        "launch_ms_p10_p50_p90": launch_percentiles(kernel_ms),
     }
     if args.rope:
         line["roofline"]["avg_call_ms_with_key_pass"] = round(float(np.mean(launch_ms)), 4)
@@ -347,6 +354,7 @@ def bench_fp8(args, torch, fa, w: si.Workload) -> int:
         "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fa_fwd_fp8_kernel",
         "avg_launch_ms": round(avg_ms, 4),
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
     line["kernel_source_sha256"] = kernel_source_hash(FP8_SOURCES)
     if not args.no_cpu_baseline:
@@ -413,6 +421,7 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
         "kernel": "fa_bwd (fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, fa_bwd_dq_kernel)",
         "avg_launch_ms": round(avg_ms, 4),
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
     if not args.no_cpu_baseline:
         line.update(oracle_leg("backward", w, inp, {"dout_bits": dout_bits,
@@ -457,6 +466,7 @@ def bench_splitkv(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
         "kernel": "fa_fwd_splitkv (fa_splitkv_kernel + fa_splitkv_merge_kernel)",
         "avg_launch_ms": round(avg_ms, 4),
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
+        "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
     line["kernel_source_sha256"] = kernel_source_hash(SPLITKV_SOURCES)
     if not args.no_cpu_baseline:

@@ -55,6 +55,9 @@ def test_headline_bench_line_carries_the_contract():
     assert 0.0 < roof["achieved"] < roof["peak"]
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-3)
     assert roof["traffic"] is None or roof["traffic"] > 0
+    lo, hi = roof["launch_ms_min_max"]
+    p10, p50, p90 = roof["launch_ms_p10_p50_p90"]
+    assert lo <= p10 <= p50 <= p90 <= hi
 
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s"
