@@ -499,9 +499,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads would shard across GPUs with no communication; see the design notes)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: libfa has no multi-GPU path (heads would shard "
+              "across GPUs with no communication between them)", file=sys.stderr)
         return 2
 
     import torch
