@@ -31,6 +31,10 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak, N=16K d=128 causal bf16"
 # MI355X published dense matrix peaks (TFLOP/s), per input type
 MFMA_PEAK_TFLOPS = {si.BF16: 2500.0, si.F16: 2500.0, "e4m3": 5000.0}
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+# Transcendental issue ceiling: v_exp_f32 occupies a SIMD's vector ALU for 16 cycles per 64-lane
+# instruction (measured with a single-SIMD issue probe), so 256 CUs x 4 SIMDs x 64 / 16 lanes
+# per cycle at the 2.4 GHz peak clock.
+EXP2_PEAK_PER_S = 256 * 4 * 64 / 16 * 2.4e9
 KERNEL_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_fwd.hip",
                   "exact_tiled_attention_39_amd/csrc/fa_device.h"]
 SPLITKV_SOURCES = ["exact_tiled_attention_39_amd/csrc/fa_splitkv.hip",
@@ -65,52 +69,65 @@ def cpu_baseline(w: si.Workload, inp, seconds: float, bytes_metric: bool = False
                  arrays=None) -> dict:
     """The fp64 oracle, as it stands, on seeded query rows until the time budget is spent.
 
+    Q, K and V are decoded to float64 once, before the clock starts, so the timed region holds
+    only the oracle's own work (oracle.attention_rows). The sampled rows are taken head by head
+    (32 rows of one head per call, heads in a seeded order), so each call upcasts nothing.
     Reported in TFLOP/s (4*keys*d per row), or with bytes_metric in GB/s: the rows' share of
     the workload's FLOPs times the workload's minimum bytes, per second."""
     import oracle
     from threadpoolctl import threadpool_info
 
     if arrays is None:
-        arrays = tuple(si.bits_to_f64(x, w.dtype).astype(np.float32) for x in (inp.q, inp.k, inp.v))
-    q, k, v = arrays
+        arrays = tuple(si.bits_to_f64(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in arrays)
     total_rows = w.batch * w.heads_q * w.seqlen
-    if total_rows <= 4096:  # few query rows (decode): every row, in seeded order
+    if total_rows <= 4096:  # few query rows (decode): every row
         rows = [(b, h, t) for b in range(w.batch) for h in range(w.heads_q)
                 for t in range(w.seqlen)]
     else:
-        rows = si.sample_rows(w, 1 / 64, seed=1234)
-    order = np.random.default_rng(99).permutation(len(rows))
-    rows = [rows[i] for i in order]
+        rows = si.sample_rows(w, 1 / 4, seed=1234)  # more than the budget: stops at `seconds`
+    by_head = {}
+    for r in rows:
+        by_head.setdefault((r[0], r[1]), []).append(r)
+    heads = list(by_head)
+    order = np.random.default_rng(99).permutation(len(heads))
+    chunks = []
+    for i in order:
+        hr = by_head[heads[i]]
+        chunks += [hr[j:j + 32] for j in range(0, len(hr), 32)]
     cu, cu_k = inp.cu_seqlens, inp.cu_seqlens_k
     starts = cu[:-1] if cu is not None else None
-    done, flops = 0, 0.0
-    t0 = time.perf_counter()
-    while done < len(rows) and time.perf_counter() - t0 < seconds:
-        chunk = rows[done:done + 32]
+
+    def row_flops(i):
+        if cu is not None:
+            s = int(np.searchsorted(starts, i, side="right")) - 1
+            while cu[s + 1] <= i:
+                s += 1
+            s0, s1 = int(cu[s]), int(cu[s + 1])
+        else:
+            s, s0, s1 = 0, 0, w.seqlen
+        if cu is None:
+            nk = w.keys
+        elif cu_k is not None:
+            nk = int(cu_k[s + 1] - cu_k[s])
+        else:
+            nk = s1 - s0
+        shift = nk - (s1 - s0)  # the queries are the last positions of the keys
+        keys = min(nk, i - s0 + shift + 1) if w.causal else nk
+        return 4.0 * max(keys, 0) * w.head_dim
+
+    done, flops, elapsed = 0, 0.0, 0.0
+    for chunk in chunks:
+        if elapsed >= seconds:
+            break
+        t0 = time.perf_counter()
         oracle.attention_rows(q, k, v, w.scale, w.causal, chunk, cu_seqlens=cu,
                               cu_seqlens_k=cu_k)
-        for _, _, i in chunk:
-            if cu is not None:
-                s = int(np.searchsorted(starts, i, side="right")) - 1
-                while cu[s + 1] <= i:
-                    s += 1
-                s0, s1 = int(cu[s]), int(cu[s + 1])
-            else:
-                s, s0, s1 = 0, 0, w.seqlen
-            # keys of the row's sequence
-            if cu is None:
-                nk = w.keys
-            elif cu_k is not None:
-                nk = int(cu_k[s + 1] - cu_k[s])
-            else:
-                nk = s1 - s0
-            shift = nk - (s1 - s0)  # the queries are the last positions of the keys
-            keys = min(nk, i - s0 + shift + 1) if w.causal else nk
-            flops += 4.0 * max(keys, 0) * w.head_dim
+        elapsed += time.perf_counter() - t0
+        flops += sum(row_flops(i) for _, _, i in chunk)
         done += len(chunk)
-    elapsed = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
+    blas = max([p.get("num_threads", 1) for p in threadpool_info()
+                if p.get("user_api") == "blas"] or [1])
     if bytes_metric:
         value, unit = flops / w.flops() * w.io_bytes() / elapsed / 1e9, "GB/s"
     else:
@@ -118,14 +135,73 @@ def cpu_baseline(w: si.Workload, inp, seconds: float, bytes_metric: bool = False
     return {
         "value": value,
         "unit": unit,
-        "cores": int(threads),
+        "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(blas),
         "kind": "oracle",
         "sample": (f"{done} seeded query rows of {total_rows} ({done / total_rows:.2e} of the "
-                   f"workload), {elapsed:.1f} s, fp64, "
+                   f"workload), 32 rows of one head per oracle call, {elapsed:.1f} s of oracle "
+                   f"time (inputs decoded to fp64 beforehand, untimed), fp64, "
                    + ("rows weighted by their share of the workload's FLOPs (4*keys*d), "
                       "times its minimum bytes" if bytes_metric else
                       "same FLOP convention per row (4*keys*d)")),
     }
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (the active level of pp_dpm_sclk) and board power
+    (hwmon power1_input) from sysfs every 20 ms while the timed launches run. Reports null
+    fields where the files are not readable or several cards are visible."""
+
+    def __init__(self):
+        import glob
+        import threading
+
+        self.sclk_files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.power_files = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read_mhz(path):
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    return float(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                if len(self.sclk_files) == 1:
+                    v = self._read_mhz(self.sclk_files[0])
+                    if v is not None:
+                        self.mhz.append(v)
+                if len(self.power_files) == 1:
+                    with open(self.power_files[0]) as f:
+                        self.watts.append(float(f.read().strip()) / 1e6)
+            except OSError:
+                pass
+            self._stop.wait(0.02)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self) -> dict:
+        out = {"samples": len(self.mhz), "source": "sysfs pp_dpm_sclk active level, hwmon power1_input"}
+        if self.mhz:
+            q = np.percentile(self.mhz, [10, 50, 90])
+            out["sclk_mhz_p10_p50_p90"] = [round(float(x)) for x in q]
+        else:
+            out["sclk_mhz_p10_p50_p90"] = None
+        out["board_power_w_mean"] = round(float(np.mean(self.watts)), 1) if self.watts else None
+        return out
 
 
 def copy_calibration(torch, mib: int) -> int:
@@ -144,7 +220,8 @@ def copy_calibration(torch, mib: int) -> int:
 
 def time_calls(torch, step, warmup: int, steps: int):
     """Warm-up calls, then `steps` timed calls: (wall ms per call over the timed region, list
-    of per-call HIP-event ms recorded on torch's current stream, where libfa launches)."""
+    of per-call HIP-event ms recorded on torch's current stream, where libfa launches). The
+    clock and power samples of the timed region are left in time_calls.clocks."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -152,13 +229,15 @@ def time_calls(torch, step, warmup: int, steps: int):
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in events:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for a, b in events:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    time_calls.clocks = clocks.summary()
     return (t1 - t0) * 1e3 / steps, [a.elapsed_time(b) for a, b in events]
 
 
@@ -215,7 +294,31 @@ def oracle_leg(kind: str, w: si.Workload, inp: si.Inputs, gpu: dict, args) -> di
         "rows": len(rows),
         "max_abs_dO": float(np.abs(o_gpu - o_ref).max()),
         "max_lse_err": float((np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1)).max()),
+        "max_abs_dO_by_abs_O_ref": band_errors(o_gpu, o_ref, w.dtype),
     }
+    return out
+
+
+# |O_ref| bands for the error breakdown: rounding the output alone costs up to half a unit of
+# the output type, so a band's error is read against half a unit at its largest |O_ref|.
+BAND_EDGES = [0.5, 1.0, 2.0, 4.0, 8.0]
+
+
+def band_errors(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str) -> list:
+    """Max |dO| and element count per |O_ref| band, with half an output unit at the band's
+    largest |O_ref| (significand of 8 bits for bf16, 11 for fp16)."""
+    mant = 8 if dtype == si.BF16 else 11
+    edges = [0.0] + BAND_EDGES + [np.inf]
+    err = np.abs(o_gpu - o_ref).ravel()
+    mag = np.abs(o_ref).ravel()
+    out = []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        sel = (mag >= lo) & (mag < hi)
+        if sel.any():
+            top = float(mag[sel].max())
+            half_unit = float(2.0 ** (np.floor(np.log2(top)) - mant)) if top > 0 else 0.0
+            out.append({"band": [lo, hi if np.isfinite(hi) else None], "n": int(sel.sum()),
+                        "max_abs_dO": float(err[sel].max()), "half_unit_at_max": half_unit})
     return out
 
 
@@ -306,6 +409,17 @@ def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
     }
     if args.rope:
         line["roofline"]["avg_call_ms_with_key_pass"] = round(float(np.mean(launch_ms)), 4)
+    # secondary bound: one exponential per visible score (flops / (4 d) by the convention)
+    exps = flops / (4.0 * w.head_dim)
+    line["exp2_bound"] = {
+        "exps_per_launch": exps,
+        "achieved_per_s": exps / (avg_kernel_ms * 1e-3),
+        "peak_per_s": EXP2_PEAK_PER_S,
+        "frac": round(exps / (avg_kernel_ms * 1e-3) / EXP2_PEAK_PER_S, 4),
+        "note": "v_exp_f32 issue ceiling; the kernel also issues about 3 full-rate VALU "
+                "instructions per score (scale-and-shift FMA, row sums, conversion to the input type)",
+    }
+    line["gpu_clocks"] = time_calls.clocks
     line["kernel_source_sha256"] = kernel_source_hash()
     if not args.no_cpu_baseline:
         gpu.update(o_bits=bits(o, torch), lse=lse.cpu().numpy().astype(np.float64))
@@ -356,6 +470,7 @@ def bench_fp8(args, torch, fa, w: si.Workload) -> int:
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
         "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
+    line["gpu_clocks"] = time_calls.clocks
     line["kernel_source_sha256"] = kernel_source_hash(FP8_SOURCES)
     if not args.no_cpu_baseline:
         import oracle
@@ -423,6 +538,7 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
         "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
+    line["gpu_clocks"] = time_calls.clocks
     if not args.no_cpu_baseline:
         line.update(oracle_leg("backward", w, inp, {"dout_bits": dout_bits,
                                                     "dq_bits": bits(dq, torch)}, args))
@@ -468,6 +584,7 @@ def bench_splitkv(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
         "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
     }
+    line["gpu_clocks"] = time_calls.clocks
     line["kernel_source_sha256"] = kernel_source_hash(SPLITKV_SOURCES)
     if not args.no_cpu_baseline:
         line.update(oracle_leg("splitkv", w, inp, {"o_bits": bits(o, torch),

@@ -28,8 +28,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int N>
 using Int = std::integral_constant<int, N>;
 
-// Per input type: v_mfma_f32_32x32x16 on 8-element operands, ds_read_b64_tr_b16, and the
-// round-to-nearest-even pack of two fp32 values.
+// Per input type: v_mfma_f32_32x32x16 on 8-element operands, ds_read_b64_tr_b16, the
+// round-to-nearest-even pack of two fp32 values, and the sum of a packed pair added to an fp32
+// value (v_dot2c_f32_{bf16,f16} against (1, 1): both products are exact).
 template <bool BF16>
 struct Elem;
 
@@ -49,6 +50,10 @@ struct Elem<true> {
   static __device__ __forceinline__ float to_f32(uint16_t bits) {
     return __builtin_bit_cast(float, uint32_t(bits) << 16);
   }
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
 };
 
 template <>
@@ -66,6 +71,10 @@ struct Elem<false> {
   }
   static __device__ __forceinline__ float to_f32(uint16_t bits) {
     return float(__builtin_bit_cast(_Float16, bits));
+  }
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
+                                  __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
   }
 };
 

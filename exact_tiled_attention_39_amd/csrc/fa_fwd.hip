@@ -28,10 +28,14 @@
 //    Each tile is stored fragment-major: every 1 KB block holds exactly one MFMA operand in
 //    lane order, so every LDS read in the loop is contiguous (free of bank conflicts) and is a
 //    per-lane base plus an immediate. Out-of-range rows read as zero (ragged tails).
-//  * Running maxima are raised lazily: a tile is exponentiated against the current reference
-//    maximum and only if some lane's sum exceeds 2^15 (a score that far above the reference,
-//    or the first tile) is the tile maximum formed and O, l rescaled. Any reference maximum
+//  * Running maxima are raised lazily: the first tile's maximum is the reference; a later tile
+//    is exponentiated against the current reference and only if some lane's sum exceeds 2^15
+//    (a score that far above the reference) is the tile maximum formed and O, l rescaled. Any reference maximum
 //    gives the same O = O~ / l and LSE = m + log2(l); the bound keeps each exp2 <= 2^15.
+//  * Two row sums: l of the fp32 exponentials gives the LSE, and l~ of the same values rounded
+//    to the input type (the weights the P V product actually uses) normalises O, so the output
+//    is an exact convex combination of V rows. With a lazily raised reference the dominant
+//    weight is rarely exactly 1, and normalising by l would leave its rounding error in O.
 //  * exp is exp2 with scale * log2(e) folded into one FMA per score.
 //  * Causal blocks stop at the diagonal; only diagonal and ragged-tail tiles are masked.
 //    Causal blocks are aligned to the sequence end, so a partial block is the cheapest one.
@@ -269,7 +273,8 @@ void fa_fwd_kernel(const KernelArgs p) {
   const unsigned char* rd_v = lds_v + lane * 8;
 
   float m_run = -INFINITY;  // reference maximum of scaled scores, log2 units (Theorem 2's m)
-  float l_run = 0.f;        // running sum of this half-wave's keys (Theorem 2's l)
+  float l_run = 0.f;        // running sum of this half-wave's keys (Theorem 2's l), for the LSE
+  float lr_run[4] = {0.f, 0.f, 0.f, 0.f};  // the same sum of the rounded P~, O's normaliser
   f32x16 oacc[kOBlocks];    // unnormalised O^T: lane holds head-dims of its query column
 #pragma unroll
   for (int j = 0; j < kOBlocks; ++j) oacc[j] = f32x16{};
@@ -362,8 +367,8 @@ void fa_fwd_kernel(const KernelArgs p) {
     }
     f32x16 ex[2];
     float part[4];
-    auto expo = [&]() __attribute__((always_inline)) {
-      const float neg_m = -m_run;
+    auto expo = [&](float m_ref) __attribute__((always_inline)) {
+      const float neg_m = -m_ref;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -375,23 +380,32 @@ void fa_fwd_kernel(const KernelArgs p) {
             part[i & 3] += ex[kb][i];
         }
     };
-    expo();
-    float rsum = (part[0] + part[1]) + (part[2] + part[3]);
-    // Rare path: the first tile (no reference yet), or a score far above the reference.
-    // NaN sums also land here; they propagate to the output either way.
-    if (__builtin_amdgcn_ballot_w64(!(rsum <= kLazyBound))) {
+    auto tile_max = [&]() __attribute__((always_inline)) {
       float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      const float m_new = fmaxf(m_run, fmaxf(mx, __shfl_xor(mx, 32)) * p.c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+      return fmaxf(mx, __shfl_xor(mx, 32)) * p.c;
+    };
+    // First tile: its own maximum is the reference (O and the sums are still zero). Every row
+    // that sees any key sees one in the first tile of its sequence, so a row whose reference
+    // stays -inf sees no key at all; its NaN sums take the rare path and are never stored.
+    if (tile == 0) m_run = tile_max();
+    expo(m_run);
+    float rsum = (part[0] + part[1]) + (part[2] + part[3]);
+    // Rare path: a score far above the reference. NaN sums also land here; they propagate to
+    // the output either way.
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= kLazyBound))) {
+      const float m_new = fmaxf(m_run, tile_max());
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
+      for (int e = 0; e < 4; ++e) lr_run[e] *= alpha;
+#pragma unroll
       for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
-      expo();
+      expo(m_run);
       rsum = (part[0] + part[1]) + (part[2] + part[3]);
     }
     l_run += rsum;
@@ -401,8 +415,10 @@ void fa_fwd_kernel(const KernelArgs p) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e) {
           pb[kb][tt][e] = E::pack(ex[kb][8 * tt + 2 * e], ex[kb][8 * tt + 2 * e + 1]);
+          lr_run[e] = E::add_pair(pb[kb][tt][e], lr_run[e]);
+        }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -480,13 +496,15 @@ void fa_fwd_kernel(const KernelArgs p) {
     }
   }
 
-  // ---- epilogue: O = O~ / l, LSE = ln(l) + m; both half-waves hold partial sums --------
+  // ---- epilogue: O = O~ / l~, LSE = ln(l) + m; both half-waves hold partial sums -------
   if (wrow0 >= slen || wrow0 + 32 <= 0) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float lr_half = (lr_run[0] + lr_run[1]) + (lr_run[2] + lr_run[3]);
+  const float lr_tot = lr_half + __shfl_xor(lr_half, 32);
   if (qrow >= 0 && qrow < slen) {
     // a row that sees no key: O = 0, LSE = -inf (its sums are 0 or NaN and are not used)
     const bool empty = (CAUSAL ? min(klen, qrow + shift + 1) : klen) <= 0;
-    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float inv = empty ? 0.f : 1.f / lr_tot;
     uint16_t* orow = p.o + bidx * p.o_sb + h * p.o_sh + int64_t(seq0 + qrow) * p.o_sn;
 #pragma unroll
     for (int j = 0; j < kOBlocks; ++j) {

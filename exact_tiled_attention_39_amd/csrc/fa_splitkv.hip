@@ -196,7 +196,8 @@ void fa_splitkv_kernel(const SplitArgs p) {
   const int t_first = row0 / p.group;  // smallest token of the block
 
   float m_run = -INFINITY;  // running maximum of scaled scores, log2 units
-  float l_run = 0.f;        // this half-wave's running sum
+  float l_run = 0.f;        // this half-wave's running sum (for the log-sum-exp)
+  float lr_run = 0.f;       // the same of P~ rounded to the input type (O's normaliser)
   f32x16 oacc[kOBlocks];
 #pragma unroll
   for (int j = 0; j < kOBlocks; ++j) oacc[j] = f32x16{};
@@ -252,6 +253,7 @@ void fa_splitkv_kernel(const SplitArgs p) {
       sum += ex[e];
     }
     l_run = l_run * alpha + sum;
+    lr_run *= alpha;
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < kOBlocks; ++j) oacc[j] *= alpha;
@@ -261,7 +263,10 @@ void fa_splitkv_kernel(const SplitArgs p) {
     for (int tt = 0; tt < 2; ++tt) {
       u32x4 pb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pb[e] = E::pack(ex[8 * tt + 2 * e], ex[8 * tt + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = E::pack(ex[8 * tt + 2 * e], ex[8 * tt + 2 * e + 1]);
+        lr_run = E::add_pair(pb[e], lr_run);
+      }
 #pragma unroll
       for (int j = 0; j < kOBlocks; ++j) {
         const unsigned char* base = rd_v + so + (tt * kOBlocks + j) * 1024;
@@ -277,12 +282,15 @@ void fa_splitkv_kernel(const SplitArgs p) {
   }
 
   // ---- epilogue -----------------------------------------------------------------------
+  // O~ is normalised by the sum of the rounded weights it was built from (an exact convex
+  // combination of V rows); the log-sum-exp takes the fp32 sum
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float lr_tot = lr_run + __shfl_xor(lr_run, 32);
   if (!row_ok) return;
   // no key of this split is visible to the row
   const bool empty = n == 0 || t_begin * kTileKeys > row_lim;
   const int64_t ridx = (int64_t(bidx) * p.heads_q + hq) * p.seqlen + seq0 + tq;
-  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float inv = empty ? 0.f : 1.f / lr_tot;
   const float lse2 = m_run + __builtin_amdgcn_logf(l_tot);  // log2 units
   if (p.splits == 1) {
     uint16_t* orow = p.o + bidx * p.o_sb + hq * p.o_sh + int64_t(seq0 + tq) * p.o_sn;

@@ -57,6 +57,8 @@ def errors(o, lse, o_ref, lse_ref):
     empty = np.isneginf(lse_ref)
     if not np.array_equal(np.isneginf(lse), empty) or np.isposinf(lse).any():
         return float("inf"), float("inf")
+    if empty.any() and (o[empty] != 0).any():
+        return float("inf"), float("inf")
     do = float(np.abs(o - o_ref).max()) if o.size else 0.0
     lf, lr = lse[~empty], lse_ref[~empty]
     dl = float((np.abs(lf - lr) / np.maximum(np.abs(lr), 1.0)).max()) if lf.size else 0.0

@@ -63,5 +63,16 @@ def test_headline_bench_line_carries_the_contract():
     assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s"
     assert cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
 
+    assert cpu["blas_threads"] >= 1
+
     par = line["parity"]
     assert par["max_abs_dO"] <= 1.6e-2 and par["max_lse_err"] <= 1e-5
+    bands = par["max_abs_dO_by_abs_O_ref"]
+    assert sum(b["n"] for b in bands) == par["rows"] * 128
+    assert max(b["max_abs_dO"] for b in bands) == pytest.approx(par["max_abs_dO"])
+
+    ex = line["exp2_bound"]
+    assert ex["exps_per_launch"] == flop / (4 * 128)
+    assert 0.0 < ex["frac"] < 1.0
+    assert ex["achieved_per_s"] == pytest.approx(ex["exps_per_launch"] / (roof["avg_launch_ms"] * 1e-3))
+    assert "gpu_clocks" in line and "samples" in line["gpu_clocks"]
