@@ -6,7 +6,8 @@ raises ``FaError`` on any non-OK status. There is no fallback: if the library is
 import of the binding functions raises.
 
 The C entry points (include/fa.h) are mirrored with the same names:
-``fa_fwd``, ``fa_check_args``, ``fa_splitkv_plan``, ``fa_fwd_splitkv``, ``fa_bwd``,
+``fa_fwd``, ``fa_check_args``, ``fa_splitkv_plan``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_noalloc``, ``fa_bwd``,
 ``fa_bwd_check_args``, ``fa_status_string``, ``fa_abi_version``, ``fa_params_size``,
 ``fa_bwd_params_size``. ``attention`` allocates O and LSE and calls ``fa_fwd``;
 ``attention_splitkv`` allocates O, LSE and the split workspace and calls ``fa_fwd_splitkv``;
@@ -26,9 +27,10 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 
 FA_F16, FA_BF16, FA_E4M3 = 0, 1, 2
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
- FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH) = range(9)
-FA_ABI_VERSION = 6
+ FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH, FA_ERR_SCRATCH) = range(10)
+FA_ABI_VERSION = 7
 FA_MAX_SPLITS = 256
+FA_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _I64x3 = ctypes.c_int64 * 3
 
@@ -153,6 +155,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = ctypes.c_int32
     lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_uint64, ctypes.c_void_p]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int32
+    lib.fa_fwd_splitkv_noalloc.argtypes = [ctypes.POINTER(FaFwdParams), ctypes.c_int32,
+                                           ctypes.c_void_p]
     lib.fa_bwd_params_size.restype = ctypes.c_uint32
     lib.fa_bwd_params_size.argtypes = []
     lib.fa_bwd_check_args.restype = ctypes.c_int32
@@ -402,6 +407,32 @@ def fa_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         st = int(lib.fa_fwd_splitkv(ctypes.byref(p), int(num_splits), ctypes.c_void_p(ws_ptr),
                                     ctypes.c_uint64(ws_bytes), ctypes.c_void_p(s.cuda_stream)))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+
+
+def fa_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                           lse: torch.Tensor, *, scale: float, causal: bool = False,
+                           num_splits: int = 0, cu_seqlens: Optional[torch.Tensor] = None,
+                           max_seqlen: Optional[int] = None,
+                           stream: Optional[torch.cuda.Stream] = None,
+                           cu_seqlens_k: Optional[torch.Tensor] = None,
+                           rope_cos: Optional[torch.Tensor] = None,
+                           rope_sin: Optional[torch.Tensor] = None,
+                           rope_interleaved: bool = False,
+                           k_rot: Optional[torch.Tensor] = None) -> None:
+    """Enqueues the split-KV forward writing o and lse, with the split partials in the
+    library's static per-GPU scratch instead of a workspace (nothing is allocated)."""
+    lib = load_library()
+    for t in (q, k, v, o, lse):
+        if not t.is_cuda:
+            raise ValueError("libfa runs on the GPU: all tensors must be on a HIP device")
+    p = make_params(q, k, v, o, lse, scale, causal, cu_seqlens, max_seqlen, cu_seqlens_k,
+                    rope_cos, rope_sin, rope_interleaved, k_rot)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = int(lib.fa_fwd_splitkv_noalloc(ctypes.byref(p), int(num_splits),
+                                            ctypes.c_void_p(s.cuda_stream)))
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
 

@@ -153,6 +153,27 @@ fa_status fa_fwd_splitkv(const fa_fwd_params* p, int32_t num_splits, void* works
   return ls;
 }
 
+fa_status fa_fwd_splitkv_noalloc(const fa_fwd_params* p, int32_t num_splits, void* stream) {
+  fa::SplitPlan plan;
+  const fa_status st = checked_plan(p, num_splits, &plan);
+  if (st != FA_OK) return st;
+  if (plan.workspace_bytes > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  if (p->seqlen == 0) return FA_OK;
+  if (p->cu_seqlens != nullptr && p->max_seqlen == 0) return FA_OK;
+  const char* err = nullptr;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    ws = fa::noalloc_scratch(&err);
+    if (ws == nullptr) {
+      g_last_hip_error = err;
+      return FA_ERR_LAUNCH;
+    }
+  }
+  const fa_status ls = fa::launch_forward_splitkv(*p, plan, ws, stream, &err);
+  if (ls != FA_OK && err != nullptr) g_last_hip_error = err;
+  return ls;
+}
+
 uint32_t fa_bwd_params_size(void) { return static_cast<uint32_t>(sizeof(fa_bwd_params)); }
 
 fa_status fa_bwd_check_args(const fa_bwd_params* p) {
@@ -218,6 +239,10 @@ const char* fa_status_string(int32_t status) {
              "another total length need cu_seqlens_k";
     case FA_ERR_ABI: return "FA_ERR_ABI: struct_size does not match sizeof(fa_fwd_params)";
     case FA_ERR_LAUNCH: return g_last_hip_error;
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the split partials need more than the library's static scratch "
+             "(FA_NOALLOC_SCRATCH_BYTES = 16 MiB); use fa_fwd_splitkv with a workspace, or "
+             "fewer splits";
     default: return "unknown fa_status";
   }
 }

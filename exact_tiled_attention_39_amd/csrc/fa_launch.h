@@ -35,6 +35,10 @@ SplitPlan plan_splitkv(const fa_fwd_params& p, int32_t num_splits);
 fa_status launch_forward_splitkv(const fa_fwd_params& p, const SplitPlan& plan, void* workspace,
                                  void* stream, const char** hip_error);
 
+// Device address of the current device's static split-KV scratch (FA_NOALLOC_SCRATCH_BYTES),
+// looked up once per device; NULL (and *hip_error set) on a HIP error.
+void* noalloc_scratch(const char** hip_error);
+
 // Enqueues the three backward kernels for arguments that fa_bwd_check_args already accepted.
 fa_status launch_backward(const fa_bwd_params& p, void* stream, const char** hip_error);
 

@@ -28,10 +28,17 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_device.h"
 #include "fa_launch.h"
+
+// Split partials of fa_fwd_splitkv_noalloc, for callers that cannot allocate device memory.
+// Every GPU the library runs on holds its own copy of this array until the process ends, and
+// every call on that GPU reuses it. In host code `scratch` is only a stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace fa {
 namespace {
@@ -404,6 +411,34 @@ hipError_t launch_split_mode(const SplitArgs& a, int grid, bool causal, bool var
 }
 
 }  // namespace
+
+void* noalloc_scratch(const char** hip_error) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *hip_error = hipGetErrorString(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *hip_error = "device index beyond the 64 the split-KV scratch table holds";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current: this device's copy of the array
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *hip_error = e != hipSuccess ? hipGetErrorString(e) : "hipGetSymbolAddress returned NULL";
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
 
 SplitPlan plan_splitkv(const fa_fwd_params& p, int32_t num_splits) {
   SplitPlan plan;

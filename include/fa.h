@@ -32,8 +32,9 @@
  * probabilities are rounded to the input type (round to nearest even) before the P V product;
  * O is rounded to the input type (round to nearest even); LSE is fp32.
  *
- * Threading and memory: libfa allocates nothing and keeps no state; every call only enqueues
- * work on the given HIP stream and returns. The caller owns every buffer.
+ * Threading and memory: libfa allocates nothing and keeps no state (apart from the static
+ * scratch array of fa_fwd_splitkv_noalloc and its per-device address table); every call only
+ * enqueues work on the given HIP stream and returns. The caller owns every buffer.
  */
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -68,7 +69,9 @@ typedef enum fa_status {
                              cu_seqlens_k without cu_seqlens; or packed queries whose keys
                              differ in length without cu_seqlens_k */
   FA_ERR_ABI = 7,         /* struct_size does not match this library's fa_fwd_params */
-  FA_ERR_LAUNCH = 8       /* the HIP launch failed (the HIP error text is kept per thread) */
+  FA_ERR_LAUNCH = 8,      /* the HIP launch failed (the HIP error text is kept per thread) */
+  FA_ERR_SCRATCH = 9      /* fa_fwd_splitkv_noalloc: the split partials would exceed
+                             FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -279,6 +282,27 @@ fa_status fa_splitkv_plan(const fa_fwd_params* p, int32_t num_splits, int32_t* s
  */
 fa_status fa_fwd_splitkv(const fa_fwd_params* p, int32_t num_splits, void* workspace,
                          uint64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_splitkv for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, kernels and results as
+ * fa_fwd_splitkv, but the split partials go to a static device array that the library holds
+ * (one per GPU, FA_NOALLOC_SCRATCH_BYTES, kept until the process ends) instead of a caller
+ * workspace; the call itself allocates nothing. The caller still owns q, k, v, o, lse (and
+ * k_rot). The array's device address is looked up on the first call on each device (with that
+ * device current; the stream must belong to the current device).
+ *
+ * Every call on one GPU shares its array and overwrites it: calls that may overlap on one GPU
+ * (different streams, or different host threads without ordering) race and can corrupt each
+ * other's results; order them on one stream. Nothing in the array has to start at zero, and
+ * no earlier contents reach an output.
+ *
+ * Errors: those of fa_splitkv_plan; FA_ERR_SCRATCH when the planned workspace exceeds
+ * FA_NOALLOC_SCRATCH_BYTES (splits x batch x heads_q x seqlen x (head_dim + 1) x 4 bytes), all
+ * before any device call; FA_ERR_LAUNCH if the address lookup or a launch fails.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+fa_status fa_fwd_splitkv_noalloc(const fa_fwd_params* p, int32_t num_splits, void* stream);
 
 /* sizeof(fa_bwd_params) as compiled into the library. */
 uint32_t fa_bwd_params_size(void);

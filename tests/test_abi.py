@@ -22,8 +22,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_check_args",
                                     "fa_bwd_params_size", "fa_check_args", "fa_fwd",
-                                    "fa_fwd_splitkv", "fa_params_size", "fa_splitkv_plan",
-                                    "fa_status_string"]
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_params_size",
+                                    "fa_splitkv_plan", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -256,8 +256,25 @@ def test_splitkv_workspace_errors_before_any_device_call():
     assert lib.fa_fwd_splitkv(ctypes.byref(empty), 4, None, 0, None) == fa.FA_OK
 
 
+def test_noalloc_errors_before_any_device_call():
+    lib = fa.load_library()
+    p = decode_params()
+    # the workspace of 256 splits is past the static scratch: refused, nothing launched
+    _, need = fa.fa_splitkv_plan(p, 256)
+    assert need > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(p), 256, None) == fa.FA_ERR_SCRATCH
+    # argument errors of fa_fwd and of the plan come first
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(decode_params(heads_kv=3)), 4,
+                                      None) == fa.FA_ERR_GQA
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(p), -1, None) == fa.FA_ERR_SHAPE
+    assert lib.fa_fwd_splitkv_noalloc(None, 0, None) == fa.FA_ERR_NULL
+    empty = decode_params(seqlen=0, q=0, o=0, lse=0)
+    assert lib.fa_fwd_splitkv_noalloc(ctypes.byref(empty), 4, None) == fa.FA_OK
+    assert "16 MiB" in fa.fa_status_string(fa.FA_ERR_SCRATCH)
+
+
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         text = fa.fa_status_string(s)
         assert text and (s == fa.FA_ERR_LAUNCH or text.startswith("FA_"))
     assert fa.fa_status_string(1234) == "unknown fa_status"
