@@ -19,7 +19,7 @@ LIB = PKG / "libfa.so"
 
 ARCH = "gfx950"
 SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_splitkv.hip", "fa_rope.hip", "fa_bwd.hip",
-           "fa_api.cpp"]
+           "fa_api.cpp", "fa_plan.cpp"]
 # Per-source extra flags. The backward kernels run one wave per SIMD with more live state than
 # the 256 VALU-addressable registers: the VGPR form of every MFMA keeps S, dP and the
 # accumulators where the element-wise code reads them, and the accumulation registers then

@@ -1,5 +1,6 @@
-// Internal interface between the C-ABI entry points (fa_api.cpp) and the HIP kernels
-// (fa_fwd.hip, fa_bwd.hip). Not installed; callers use include/fa.h.
+// Internal interface between the C-ABI entry points (fa_api.cpp, fa_plan.cpp) and the HIP
+// kernels (fa_fwd.hip, fa_bwd.hip, ...). Not installed; callers use include/fa.h. Everything
+// declared here is host code; fa_api.cpp and fa_plan.cpp build with a plain C++ compiler.
 #pragma once
 
 #include <cstdint>
@@ -17,6 +18,10 @@ fa_status launch_forward_fp8(const fa_fwd_params& p, void* stream, const char** 
 
 // Enqueues the RoPE pass that writes the rotated keys to p.k_rot (p.rope_cos set).
 fa_status launch_rope_keys(const fa_fwd_params& p, void* stream, const char** hip_error);
+
+// Split-KV geometry shared by the planner (fa_plan.cpp) and the kernels (fa_splitkv.hip).
+constexpr int kSplitTileKeys = 32;   // keys per K/V tile
+constexpr int kSplitBlockRows = 32;  // packed query rows per workgroup
 
 // Work decomposition of the split-KV forward for arguments that fa_check_args accepted.
 struct SplitPlan {
