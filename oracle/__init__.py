@@ -26,7 +26,9 @@ What it computes, with the passages it follows:
   the FromZero2AI page's mechanism 3 must reproduce.
 
 Every function here is pinned by tests under ``-m "not gpu"`` (worked examples, closed forms,
-invariants, a library routine, brute force); none is "parity unpinned".
+invariants, a library routine, brute force); none is "parity unpinned". One constant is an
+empirical reading: the FP8 matrix instruction's summation error in ``fp8`` (its docstring says
+how it was measured), which the FP8 score and LSE bounds scale with.
 """
 from .definition import (attention, attention_rows, kv_head, score_matrix_bytes,
                         softmax_rows_with_lse)

@@ -18,18 +18,29 @@ no recipe. The readings taken here (also listed in the design notes):
     value stays below 2^8, inside E4M3's range) and rounded to nearest even; the matrix
     instruction's block scale multiplies 2^k back exactly. The row sum l uses the unrounded
     values (l >= 2^8) and O is rounded to bf16.
-  * Error bounds. The E4M3 matrix instruction of gfx950 (32x32x64) does not add its 64 exact
-    products in full fp32: measured on MI355X over 6 million random products of full-range
-    codes, one instruction's error reached 2^-11.4 of its largest |product| (2^-14 of the sum
-    of |products|), so a score carries an error of at most e_S = |scale| (d / 64) 2^-10
-    max|q| max|k| (``score_error_bound``, 2^-10 leaving a margin of 2.6 over that maximum).
-    The log-sum-exp then errs by at most e_S beyond the forward's 1e-5 relative bound
-    (``lse_tolerance``). Rounding to E4M3 changes each weight by at most 2^-4 of itself while it
-    is a normal number, and by at most 2^(k-10) <= max(2^-10, B 2^-17) once it is subnormal, so
-    a block of 32 errs by at most max(2^-5, B 2^-12) absolutely; over the n_keys / 32 blocks of
-    a row, relative to l >= 2^8, that is at most n_keys 2^-18 + 2^-12. The score error moves
-    each weight by a factor within exp(+-2 e_S). So |dO| <= max|v| (2^-4 + n_keys 2^-18 +
-    2^-12 + 2 e_S) per row, plus half a bf16 unit of O (``o_tolerance``).
+  * Error bounds, in two parts.
+    1. The matrix instruction's sums (an empirical reading, not a derivation). The E4M3
+       matrix instruction of gfx950 (32x32x64) does not add its 64 exact products in full
+       fp32. The pages and the public ISA documents give no accumulation precision, so the
+       bound takes a measurement: an in-bounds probe on one MI355X over 6 million random
+       64-term products of full-range codes found errors up to 2^-11.4 of the largest
+       |product| (2^-14 of the sum of |products|), and 30-50 % of the sums exact. The bound
+       uses 2^-10 (a margin of 2.6): a score errs by at most e_S = |scale| (d / 64) 2^-10
+       max|q| max|k| (``score_error_bound``), the log-sum-exp by at most e_S beyond the
+       forward's 1e-5 relative bound (``lse_tolerance``), and each weight moves by a factor
+       within exp(+-2 e_S).
+    2. The rounding of the probabilities (derived, and pinned by ``simulate_attention``, the
+       reading's quantisation in float64 on exact scores). Rounding to E4M3 changes a weight by
+       at most 2^-4 of itself while it is a normal number, and by at most 2^(k-10) <=
+       max(2^-10, B 2^-17) once it is subnormal, so a block of 32 errs by at most
+       max(2^-5, B 2^-12) absolutely; over the n_keys / 32 blocks of a row, relative to
+       l >= 2^8, that is at most n_keys 2^-18 + 2^-12. Both terms are reached: a dominant
+       weight at an E4M3 rounding midpoint costs 2^-4 / (1 + 2^-4) of its V row, and blocks of
+       32 weights at subnormal midpoints, all rounding the same way, cost n_keys 2^-18 of the
+       V rows against a dominant weight of 2^8 (the tests build both).
+    So |dO| <= max|v| (2^-4 + n_keys 2^-18 + 2^-12 + 2 e_S) per row, plus half a bf16 unit of
+    O (``o_tolerance``). Random inputs stay far below it (the errors of many weights cancel),
+    so the tests also hold the kernel's mean error to that of the simulation.
 """
 from __future__ import annotations
 
@@ -55,8 +66,13 @@ def dequantize(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
     return decode_e4m3(codes) * np.asarray(descale, dtype=np.float64)[:, :, None, None]
 
 
-# One 64-term E4M3 MFMA sum errs by at most this fraction of its largest |product| (see above).
+# One 64-term E4M3 MFMA sum errs by at most this fraction of its largest |product|: an empirical
+# reading (part 1 above: the largest error measured over 6e6 sums was 2^-11.4).
 MFMA_E4M3_SUM_ERROR = 2.0 ** -10
+
+# The reading's shift of the probabilities (the row maximum's weight) and block length.
+P_SHIFT = 2.0 ** 8
+P_BLOCK = 32
 
 
 def score_error_bound(q_values: np.ndarray, k_values: np.ndarray, scale: float,
@@ -78,3 +94,62 @@ def o_tolerance(v_values: np.ndarray, n_keys: int, score_err: float = 0.0) -> fl
     """The bound above for outputs built from these V values (all heads) and n_keys keys."""
     vmax = float(np.abs(v_values).max()) if v_values.size else 0.0
     return vmax * (2.0 ** -4 + n_keys * 2.0 ** -18 + 2.0 ** -12 + 2.0 * score_err) + vmax * 2.0 ** -9
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to E4M3 with round-to-nearest-even (torch's float8_e4m3fn on the
+    CPU, a library routine independent of the kernels), returned as float64."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def block_scaled_probabilities(p: np.ndarray, quantize: bool = True) -> np.ndarray:
+    """The reading's P~ for rows of shifted probabilities p ([rows, n], float32 values, the
+    largest of a row at most 2^8 times the reference's): each block of 32 keys of a row with
+    sum B in [2^e, 2^(e+1)) is divided by 2^k, k = max(0, e - 7), rounded to E4M3 and
+    multiplied back by 2^k (exactly, as the matrix instruction's block scale does). Without
+    quantize the values are returned unchanged (float64)."""
+    p = np.asarray(p, dtype=np.float32)
+    if not quantize:
+        return p.astype(np.float64)
+    rows, n = p.shape
+    out = np.zeros((rows, n))
+    for b0 in range(0, n, P_BLOCK):
+        blk = p[:, b0:b0 + P_BLOCK]
+        bsum = blk.astype(np.float64).sum(axis=1)
+        e = np.where(bsum > 0, np.floor(np.log2(np.where(bsum > 0, bsum, 1.0))), 0.0)
+        k = np.maximum(0.0, e - 7.0)
+        scaled = (blk / np.exp2(k)[:, None].astype(np.float32)).astype(np.float32)
+        out[:, b0:b0 + P_BLOCK] = round_e4m3(scaled) * np.exp2(k)[:, None]
+    return out
+
+
+def simulate_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                       causal: bool = False, ref_offset: float = 0.0,
+                       quantize: bool = True):
+    """The FP8 reading's arithmetic on exact (float64) scores, for one head: q [n, d], k, v
+    [nk, d] (decoded values). Scores s = scale q.k in log2 units; reference m = row maximum
+    minus ref_offset (0 <= ref_offset <= 23, the range a lazily raised reference covers);
+    p = 2^(s - m + 8) rounded to float32; P~ from block_scaled_probabilities; l = sum of the
+    unrounded p; O = sum_j P~_j v_j / l; LSE = (m - 8 + log2 l) ln 2. Returns (O, LSE); rows
+    that see no key get O = 0, LSE = -inf. With quantize=False this is the definition."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, nk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T) * np.log2(np.e)
+    if causal:
+        i = np.arange(n)[:, None]
+        j = np.arange(nk)[None, :]
+        s = np.where(j <= i + (nk - n), s, -np.inf)
+    m = s.max(axis=1, initial=-np.inf)
+    seen = np.isfinite(m)
+    m_ref = np.where(seen, m - ref_offset, 0.0)
+    p = np.exp2(s - m_ref[:, None] + 8.0).astype(np.float32)
+    pt = block_scaled_probabilities(p, quantize)
+    l = p.astype(np.float64).sum(axis=1)
+    o = np.where(seen[:, None], (pt @ v) / np.where(seen, l, 1.0)[:, None], 0.0)
+    lse = np.where(seen, (m_ref - 8.0 + np.log2(np.where(seen, l, 1.0))) * np.log(2.0), -np.inf)
+    return o, lse
