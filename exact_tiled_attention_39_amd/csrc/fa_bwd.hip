@@ -289,26 +289,40 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
       TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
     ld_off[i] = int(row * ((lay & 1) ? p.do_sn : p.q_sn) * 2) + col * 2;
   }
-  auto issue = [&](auto stage, int st) __attribute__((always_inline)) {
+  // The next tile to issue, carried from step to step (step st is query tile t_first +
+  // st % per_head of query head it.h * group + st / per_head): its tile index, row pointers
+  // and LSE/D row; a change of head adds the jump to the next head's first tile.
+  const int hq0 = it.h * p.group;
+  const bool is_do = lay & 1;
+  const int64_t lay_sn = is_do ? p.do_sn : p.q_sn;
+  const int64_t lay_sh = is_do ? p.do_sh : p.q_sh;
+  const uint16_t* iss_src = (is_do ? p.dout + bidx * p.do_sb : p.q + bidx * p.q_sb) +
+                            hq0 * lay_sh + int64_t(seq0 + t_first * kTileRows) * lay_sn;
+  const int64_t src_step = int64_t(kTileRows) * lay_sn;
+  const int64_t src_jump = lay_sh - int64_t(per_head) * src_step;  // to the next head's first tile
+  int64_t iss_lrow = (int64_t(bidx) * p.heads_q + hq0) * p.seqlen + seq0 + t_first * kTileRows;
+  const int64_t lrow_jump = p.seqlen - int64_t(per_head) * kTileRows;
+  int iss_t = t_first;
+  auto issue = [&](auto stage) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
-    const int h = it.h * p.group + st / per_head;
-    const int r0 = (t_first + st % per_head) * kTileRows;
-    const int rows = min(slen - r0, kTileRows);
-    const bool is_do = lay & 1;
-    const uint16_t* src = is_do
-        ? p.dout + bidx * p.do_sb + h * p.do_sh + int64_t(seq0 + r0) * p.do_sn
-        : p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0 + r0) * p.q_sn;
-    const int64_t sn = is_do ? p.do_sn : p.q_sn;
-    const u32x4 rs = make_rsrc(src, int((rows - 1) * sn * 2) + D * 2);
+    const int rows = min(slen - iss_t * kTileRows, kTileRows);
+    const u32x4 rs = make_rsrc(iss_src, int((rows - 1) * lay_sn * 2) + D * 2);
     const uint32_t base = lds0 + ST * kStage + lay * G::kTileBytes + (wave & 1) * kPer * 1024;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     if (wave < 2) {
       // 32 fp32 rows of LSE (wave 0) or D (wave 1): lanes 0..7 carry them, the rest read 0
-      const int64_t lrow = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + r0;
-      const float* lsrc = wave == 0 ? p.lse + lrow : p.delta + lrow;
+      const float* lsrc = wave == 0 ? p.lse + iss_lrow : p.delta + iss_lrow;
       dma16(make_rsrc(lsrc, rows * 4), lds0 + ST * kStage + (wave == 0 ? kLse : kDel),
             lane * 16);
+    }
+    // advance to the next tile
+    iss_src += src_step;
+    iss_lrow += kTileRows;
+    if (++iss_t == n_qt) {
+      iss_t = t_first;
+      iss_src += src_jump;
+      iss_lrow += lrow_jump;
     }
   };
 
@@ -338,11 +352,13 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 
     // dV role, tile st in stage ST: S, P (masked; stored for the partner in slot st % 2),
     // dV^T += dO^T P
+    int cur_t = t_first;  // query tile of the dV wave's step (advanced like the issue's)
     auto dv_tile = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       const unsigned char* sb = smem + ST * kStage;
       part = chain_over_d<BF16, kSteps>(sb + kQop + lane * 16, rf);
-      const int r0 = (t_first + st % per_head) * kTileRows;
+      const int r0 = cur_t * kTileRows;
+      if (++cur_t == n_qt) cur_t = t_first;
       // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
       float lse[16], pv[16];
       read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
@@ -398,7 +414,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     // closing barrier also waits for tile st + 1.
     auto step = [&](auto stage, int st) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
-      if (st + 1 < n_steps) issue(Int<(ST + 1) % kRing>{}, st + 1);
+      if (st + 1 < n_steps) issue(Int<(ST + 1) % kRing>{});
       if constexpr (DK) {
         if (st > 0) dk_tile(Int<(ST + kRing - 1) % kRing>{}, st - 1);
       } else {
@@ -408,7 +424,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     };
 
     if (n_steps > 0) {
-      issue(Int<0>{}, 0);
+      issue(Int<0>{});
       tile_sync();
       for (int st = 0; st < n_steps; st += kRing) {
         step(Int<0>{}, st);
@@ -512,14 +528,18 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
       TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
     ld_off[i] = int(row * (lay == 1 ? p.v_sn : p.k_sn) * 2) + col * 2;
   }
-  const uint16_t* kbase = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
-  const uint16_t* vbase = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
-  auto issue = [&](auto stage, int tile) __attribute__((always_inline)) {
+  // K and V rows of the next tile to issue, carried from tile to tile
+  const uint16_t* kcur = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
+  const uint16_t* vcur = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
+  int iss_r0 = 0;
+  auto issue = [&](auto stage) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
-    const int r0 = tile * kTileRows;
-    const int rows = min(slen - r0, kTileRows);
-    const u32x4 rk = make_rsrc(kbase + int64_t(r0) * p.k_sn, int((rows - 1) * p.k_sn * 2) + D * 2);
-    const u32x4 rv = make_rsrc(vbase + int64_t(r0) * p.v_sn, int((rows - 1) * p.v_sn * 2) + D * 2);
+    const int rows = min(slen - iss_r0, kTileRows);
+    const u32x4 rk = make_rsrc(kcur, int((rows - 1) * p.k_sn * 2) + D * 2);
+    const u32x4 rv = make_rsrc(vcur, int((rows - 1) * p.v_sn * 2) + D * 2);
+    kcur += int64_t(kTileRows) * p.k_sn;
+    vcur += int64_t(kTileRows) * p.v_sn;
+    iss_r0 += kTileRows;
 #pragma unroll
     for (int i = 0; i < kPerW; ++i) {
       const int b = i * kWaves + wave;
@@ -561,14 +581,14 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
     chain_over_rows<BF16, kOBlocks>(sb + kKtr + lane * 8, pb, dqacc);
   };
 
-  issue(Int<0>{}, 0);
+  issue(Int<0>{});
   tile_sync();
   for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) issue(Int<1>{}, t + 1);
+    if (t + 1 < n_tiles) issue(Int<1>{});
     compute(Int<0>{}, t);
     tile_sync();
     if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) issue(Int<0>{}, t + 2);
+      if (t + 2 < n_tiles) issue(Int<0>{});
       compute(Int<1>{}, t + 1);
       tile_sync();
     }
