@@ -223,14 +223,19 @@ __device__ __forceinline__ void tile_sync() {
 
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
-// each, waves 4-7 dK for the same keys; a SIMD holds one of each. The dK wave runs one tile
-// behind the dV wave, so that each wave's whole tile needs one barrier: in step t the dV wave
-// forms S = Q K^T and P (masked) of tile t, hands P (fp32) to its dK partner through a
-// double-buffered LDS slot and accumulates dV^T += dO^T P; the dK wave forms dP = dO V^T of
-// tile t - 1, dS = P (dP - D) from the P handed over in step t - 1, and accumulates
-// dK^T += Q^T dS. Tiles move through a three-stage LDS ring (tiles t - 1, t and t + 1 in
-// flight). Each wave does 16 of a tile's 32 products and keeps its state within 256
-// registers; the two waves of a SIMD interleave their matrix and element-wise work freely.
+// each, waves 4-7 dK for the same keys; a SIMD holds one of each, and the two alternate, one
+// barrier-delimited phase apart, between matrix work (M phase) and element-wise work (V
+// phase), so that each SIMD overlaps one wave's exponentials or products with the other's
+// MFMAs. For query tile t (32 rows of one query head; the tiles of every query head that
+// shares the kv head follow each other):
+//   slot A_t: dV wave M: S(t+1) = Q(t+1) K^T interleaved with dV^T += dO(t)^T P(t);
+//             dK wave V: dS(t-1) = P(t-1) (dP(t-1) - D(t-1)), rounded as the B operand;
+//   slot B_t: dV wave V: P(t+1) = exp2(c S(t+1) - log2(e) L) (masked), stored in fp32 for the
+//             dK wave (two LDS slots by tile parity) and rounded as its own B operand;
+//             dK wave M: dP(t) = dO(t) V^T interleaved with dK^T += Q(t-1)^T dS(t-1).
+// Q and dO tiles, with the tile's L and D, stream through a six-stage LDS ring by direct-to-LDS
+// loads issued four tiles ahead; each is stored once, in the swizzled layout that serves both
+// its operand and its transposing reads.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -239,15 +244,17 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  constexpr int kPer = G::kBlocks / 2;  // blocks of one layout issued per wave (two per layout)
-  // stage: Q operand | dO operand | Q transposing | dO transposing | 32 LSE | 32 D (a 1 KB
-  // direct-to-LDS load each)
-  constexpr int kQop = 0, kDop = G::kTileBytes, kQtr = 2 * G::kTileBytes,
-                kDtr = 3 * G::kTileBytes, kLse = 4 * G::kTileBytes, kDel = kLse + 1024;
-  constexpr int kStage = kLse + 2048;
-  constexpr int kRing = 3;           // tile stages
-  constexpr int kPbuf = kRing * kStage;  // P of each key group, two slots of 4 x 16 fp32/lane
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage + 2 * 4 * 4096];
+  constexpr int kPer = G::kBlocks / 4;  // 1 KB blocks of its tensor a wave loads per tile
+  // Ring stage x of each tensor: Q tile at kQ + x kTileBytes, dO tile at kDo + x kTileBytes,
+  // 32 LSE at kRows + 2048 x and 32 D 1 KB after them (each a 1 KB direct-to-LDS load); each
+  // region spans less than 64 KB, so a per-lane base plus an immediate reaches every stage.
+  constexpr int kRing = 6;
+  constexpr int kAhead = 4;  // tiles issued ahead of the one whose slot A starts
+  constexpr int kQ = 0, kDo = kRing * G::kTileBytes, kRows = 2 * kRing * G::kTileBytes;
+  constexpr int kPbuf = kRows + kRing * 2048;  // P of each key group: two slots of 4 x 16 fp32/lane
+  constexpr int kPslot = 4 * 4096;
+  static_assert(kRing % 2 == 0 && kRing >= kAhead + 2, "ring stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPbuf + 2 * kPslot];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -275,31 +282,26 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   const int per_head = n_qt - t_first;
   const int n_steps = per_head * p.group;
 
-  // DMA: 4 layouts x kBlocks blocks per tile over 8 waves; wave w issues blocks
-  // [kPer (w % 2), kPer (w % 2 + 1)) of layout w / 2 (Q op, dO op, Q tr, dO tr)
-  const int lay = wave >> 1;
+  // DMA: waves 0-3 load the Q blocks of a tile, waves 4-7 the dO blocks, kPer each; waves 0
+  // and 1 also load the tile's 32 LSE and 32 D values (lanes 0..7 carry them, the rest read 0).
+  const bool is_do = role;
+  const int64_t lay_sn = is_do ? p.do_sn : p.q_sn;
+  const int64_t lay_sh = is_do ? p.do_sh : p.q_sh;
   int ld_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int blk = (wave & 1) * kPer + i;
     int row, col;
-    if (lay < 2)
-      OperandLayout::row_col(blk, lane, kSteps, row, col);
-    else
-      TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
-    ld_off[i] = int(row * ((lay & 1) ? p.do_sn : p.q_sn) * 2) + col * 2;
+    SwizzledTile::row_col((wave & 3) * kPer + i, lane, row, col);
+    ld_off[i] = int(row * lay_sn * 2) + col * 2;
   }
-  // The next tile to issue, carried from step to step (step st is query tile t_first +
-  // st % per_head of query head it.h * group + st / per_head): its tile index, row pointers
-  // and LSE/D row; a change of head adds the jump to the next head's first tile.
+  // The next tile to issue, carried from tile to tile (tile x is query tile t_first +
+  // x % per_head of query head it.h * group + x / per_head): its tile index, row pointer and
+  // LSE/D row; a change of head adds the jump to the next head's first tile.
   const int hq0 = it.h * p.group;
-  const bool is_do = lay & 1;
-  const int64_t lay_sn = is_do ? p.do_sn : p.q_sn;
-  const int64_t lay_sh = is_do ? p.do_sh : p.q_sh;
   const uint16_t* iss_src = (is_do ? p.dout + bidx * p.do_sb : p.q + bidx * p.q_sb) +
                             hq0 * lay_sh + int64_t(seq0 + t_first * kTileRows) * lay_sn;
   const int64_t src_step = int64_t(kTileRows) * lay_sn;
-  const int64_t src_jump = lay_sh - int64_t(per_head) * src_step;  // to the next head's first tile
+  const int64_t src_jump = lay_sh - int64_t(per_head) * src_step;
   int64_t iss_lrow = (int64_t(bidx) * p.heads_q + hq0) * p.seqlen + seq0 + t_first * kTileRows;
   const int64_t lrow_jump = p.seqlen - int64_t(per_head) * kTileRows;
   int iss_t = t_first;
@@ -307,16 +309,13 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     constexpr int ST = decltype(stage)::value;
     const int rows = min(slen - iss_t * kTileRows, kTileRows);
     const u32x4 rs = make_rsrc(iss_src, int((rows - 1) * lay_sn * 2) + D * 2);
-    const uint32_t base = lds0 + ST * kStage + lay * G::kTileBytes + (wave & 1) * kPer * 1024;
+    const uint32_t base = lds0 + (is_do ? kDo : kQ) + ST * G::kTileBytes + (wave & 3) * kPer * 1024;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     if (wave < 2) {
-      // 32 fp32 rows of LSE (wave 0) or D (wave 1): lanes 0..7 carry them, the rest read 0
       const float* lsrc = wave == 0 ? p.lse + iss_lrow : p.delta + iss_lrow;
-      dma16(make_rsrc(lsrc, rows * 4), lds0 + ST * kStage + (wave == 0 ? kLse : kDel),
-            lane * 16);
+      dma16(make_rsrc(lsrc, rows * 4), lds0 + kRows + ST * 2048 + wave * 1024, lane * 16);
     }
-    // advance to the next tile
     iss_src += src_step;
     iss_lrow += kTileRows;
     if (++iss_t == n_qt) {
@@ -325,136 +324,257 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
       iss_lrow += lrow_jump;
     }
   };
-
-  // P hand-off, slot t % 2: entries 4 g .. 4 g + 3 of lane L at 1 KB block g, byte 16 L
-  unsigned char* pbuf = smem + kPbuf + (wave & 3) * 4096 + lane * 16;
-  constexpr int kPslot = 4 * 4096;
-
-  // one role's loop; both roles run the same barriers
-  auto run = [&](auto role_c) __attribute__((always_inline)) {
-    constexpr bool DK = decltype(role_c)::value;
-    // resident B operand: K^T (sign of the scale applied) for the dV role, V^T for the dK role
-    u32x4 rf[kSteps];
-    if constexpr (DK) {
-      load_resident<D>(p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn, p.v_sn, kw0,
-                       slen, lane, rf);
-    } else {
-      load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0,
-                       slen, lane, rf);
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) rf[s] = (rf[s] & p.s_and) ^ p.s_xor;
-    }
-    f32x16 acc[kOBlocks];
-#pragma unroll
-    for (int j = 0; j < kOBlocks; ++j) acc[j] = f32x16{};
-    f32x16 part;   // S (dV role) or dP (dK role) of the current tile
-    u32x4 pb[2];   // P (dV role) packed as the B operand of the row contraction
-
-    // dV role, tile st in stage ST: S, P (masked; stored for the partner in slot st % 2),
-    // dV^T += dO^T P
-    int cur_t = t_first;  // query tile of the dV wave's step (advanced like the issue's)
-    auto dv_tile = [&](auto stage, int st) __attribute__((always_inline)) {
-      constexpr int ST = decltype(stage)::value;
-      const unsigned char* sb = smem + ST * kStage;
-      part = chain_over_d<BF16, kSteps>(sb + kQop + lane * 16, rf);
-      const int r0 = cur_t * kTileRows;
-      if (++cur_t == n_qt) cur_t = t_first;
-      // entry i is query row r0 + 8 (i / 4) + 4 half + i % 4
-      float lse[16], pv[16];
-      read_rows16(reinterpret_cast<const float*>(sb + kLse), half, lse);
-      const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = fmaf(part[i], p.c, lse[i] * -kLog2e);
-        if (edge) {
-          const int qrow = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool ok = qrow < slen && key < slen && (!CAUSAL || key <= qrow);
-          x = ok ? x : -INFINITY;
-        }
-        pv[i] = __builtin_amdgcn_exp2f(x);
-      }
-      unsigned char* slot = pbuf + (st & 1) * kPslot;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(slot + g * 1024) =
-            f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
-      chain_over_rows<BF16, kOBlocks>(sb + kDtr + lane * 8, pb, acc);
-    };
-    // dK role, tile st in stage ST (one step behind the dV wave): dP, dS = P (dP - D) with the
-    // P of slot st % 2, dK^T += Q^T dS
-    auto dk_tile = [&](auto stage, int st) __attribute__((always_inline)) {
-      constexpr int ST = decltype(stage)::value;
-      const unsigned char* sb = smem + ST * kStage;
-      part = chain_over_d<BF16, kSteps>(sb + kDop + lane * 16, rf);
-      float del[16];
-      read_rows16(reinterpret_cast<const float*>(sb + kDel), half, del);
-      const unsigned char* slot = pbuf + (st & 1) * kPslot;
-      float ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(slot + g * 1024);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (part[4 * g + r] - del[4 * g + r]);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
-      chain_over_rows<BF16, kOBlocks>(sb + kQtr + lane * 8, pb, acc);
-    };
-    // Step st: issue tile st + 1 (its stage last held tile st - 2, whose last reader, the dK
-    // wave in step st - 1, finished before that step's closing barrier); the dV wave runs tile
-    // st, the dK wave tile st - 1 (P of tile st - 1 was stored before the same barrier); the
-    // closing barrier also waits for tile st + 1.
-    auto step = [&](auto stage, int st) __attribute__((always_inline)) {
-      constexpr int ST = decltype(stage)::value;
-      if (st + 1 < n_steps) issue(Int<(ST + 1) % kRing>{});
-      if constexpr (DK) {
-        if (st > 0) dk_tile(Int<(ST + kRing - 1) % kRing>{}, st - 1);
-      } else {
-        dv_tile(Int<ST>{}, st);
-      }
-      tile_sync();
-    };
-
-    if (n_steps > 0) {
-      issue(Int<0>{});
-      tile_sync();
-      for (int st = 0; st < n_steps; st += kRing) {
-        step(Int<0>{}, st);
-        if (st + 1 < n_steps) step(Int<1>{}, st + 1);
-        if (st + 2 < n_steps) step(Int<2>{}, st + 2);
-      }
-      // the dK wave's last tile (its stage and P slot are not overwritten: no tile follows)
-      if constexpr (DK) {
-        const int last = n_steps - 1;
-        if (last % kRing == 0)
-          dk_tile(Int<0>{}, last);
-        else if (last % kRing == 1)
-          dk_tile(Int<1>{}, last);
-        else
-          dk_tile(Int<2>{}, last);
-      }
-    }
-    if (key < slen) {
-      if constexpr (DK)
-        store_rows<D, BF16>(p.dk + bidx * p.dk_sb + hk * p.dk_sh + int64_t(seq0 + key) * p.dk_sn,
-                            acc, p.scale, half);
+  // wait until this wave's loads of a tile are in LDS, `after` of its tiles issued later
+  auto dma_wait = [&](int after) __attribute__((always_inline)) {
+    if (wave < 2) {
+      if (after >= 2)
+        wait_vmcnt<2 * (kPer + 1)>();
+      else if (after == 1)
+        wait_vmcnt<kPer + 1>();
       else
-        store_rows<D, BF16>(p.dv + bidx * p.dv_sb + hk * p.dv_sh + int64_t(seq0 + key) * p.dv_sn,
-                            acc, 1.f, half);
+        wait_vmcnt<0>();
+    } else {
+      if (after >= 2)
+        wait_vmcnt<2 * kPer>();
+      else if (after == 1)
+        wait_vmcnt<kPer>();
+      else
+        wait_vmcnt<0>();
     }
   };
-  if (role)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  // phase boundary: a workgroup barrier that orders the P hand-off through LDS (a fence on
+  // both sides) and that the instruction scheduler may not move work across
+  auto phase_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // per-lane LDS read offsets of the swizzled tiles
+  // per-lane LDS read offsets, each with its region's start folded in and hidden from the
+  // compiler, so that it addresses every stage of a region as this base plus an immediate
+  // instead of keeping one address register per stage
+  auto lane_base = [](int off) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(off));
+    return off;
+  };
+  const int q_op0 = lane_base(kQ + SwizzledTile::operand_offset(lane, 0));
+  const int q_op1 = lane_base(kQ + SwizzledTile::operand_offset(lane, 1));
+  const int q_tr0 = lane_base(kQ + SwizzledTile::transpose_offset(lane, 0));
+  const int q_tr1 = lane_base(kQ + SwizzledTile::transpose_offset(lane, 1));
+  const int do_op0 = lane_base(kDo + SwizzledTile::operand_offset(lane, 0));
+  const int do_op1 = lane_base(kDo + SwizzledTile::operand_offset(lane, 1));
+  const int do_tr0 = lane_base(kDo + SwizzledTile::transpose_offset(lane, 0));
+  const int do_tr1 = lane_base(kDo + SwizzledTile::transpose_offset(lane, 1));
+  const int rows_rd = lane_base(kRows + 16 * half);
+  // P hand-off, slot x % 2 for tile x: entries 4 g .. 4 g + 3 of lane L at 1 KB block g,
+  // byte 16 L, of the wave's 4 KB
+  unsigned char* const pbuf = smem + lane_base(kPbuf + (wave & 3) * 4096 + lane * 16);
+
+  // resident B operand: K^T (sign of the scale applied) for the dV wave, V^T for the dK wave
+  u32x4 rf[kSteps];
+  if (role) {
+    load_resident<D>(p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn, p.v_sn, kw0,
+                     slen, lane, rf);
+  } else {
+    load_resident<D>(p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn, p.k_sn, kw0,
+                     slen, lane, rf);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) rf[s] = (rf[s] & p.s_and) ^ p.s_xor;
+  }
+  f32x16 acc[kOBlocks];  // dV^T or dK^T: lane holds head-dims of its key column
+#pragma unroll
+  for (int j = 0; j < kOBlocks; ++j) acc[j] = f32x16{};
+  f32x16 xacc = f32x16{};  // S (dV wave) or dP (dK wave) of the tile between its two phases
+  u32x4 pb[2];             // P (dV wave) or dS (dK wave), rounded: B operand of the row chain
+  pb[0] = pb[1] = u32x4{0, 0, 0, 0};
+
+  // M phase: the chain over head-dims (xacc = tile rows of `xsrc` (operand reads) . rf) and
+  // the chain over rows (acc[j] += (head-dims of block j of `ysrc`, transposing reads) . pb),
+  // interleaved one to one, each LDS operand read kAheadM MFMAs before its MFMA.
+  constexpr int kMfma = 2 * kSteps;
+  constexpr int kAheadM = 8;
+  auto phase_m = [&](auto dk_c, auto xoff, auto yoff) __attribute__((always_inline)) {
+    constexpr bool DK = decltype(dk_c)::value;  // d chain over dO, row chain over Q
+    constexpr int XO = decltype(xoff)::value;  // stage offset of the tile read by the d chain
+    constexpr int YO = decltype(yoff)::value;  // stage offset of the tile read by the row chain
+    const int x0 = DK ? do_op0 : q_op0, x1 = DK ? do_op1 : q_op1;
+    const int y0 = DK ? q_tr0 : do_tr0, y1 = DK ? q_tr1 : do_tr1;
+    u32x4 opnd[kMfma];
+    auto fetch = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value;
+      if constexpr (n % 2 == 0) {
+        constexpr int s = n / 2;
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? x1 : x0) + XO + s * 1024);
+      } else {
+        constexpr int m = n / 2, j = m % kOBlocks, tt = m / kOBlocks;
+        const u32x2 lo = E::read_tr(smem + y0 + YO + 2048 * j + 256 * tt);
+        const u32x2 hi = E::read_tr(smem + y1 + YO + 2048 * j + 256 * tt);
+        opnd[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+    auto mfma = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value;
+      if constexpr (n % 2 == 0) {
+        constexpr int s = n / 2;
+        xacc = E::mfma(opnd[n], rf[s], s == 0 ? f32x16{} : xacc);
+      } else {
+        constexpr int m = n / 2, j = m % kOBlocks, tt = m / kOBlocks;
+        acc[j] = E::mfma(opnd[n], pb[tt], acc[j]);
+      }
+    };
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      (fetch(Int<n>{}), ...);
+    }(std::make_integer_sequence<int, kAheadM>{});
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      ((
+           [&] {
+             if constexpr (n + kAheadM < kMfma) fetch(Int<n + kAheadM>{});
+             mfma(Int<n>{});
+             __builtin_amdgcn_sched_barrier(0);
+           }()),
+       ...);
+    }(std::make_integer_sequence<int, kMfma>{});
+  };
+
+  // dV wave's V phase for the tile in stage ST (P slot PS): P = exp2(c S - log2(e) L), masked
+  // where the key is past the end or above the diagonal; stored for the dK wave, rounded into pb.
+  int cur_t = t_first;  // query tile of the next V phase (advanced like the issue's)
+  auto phase_v_dv = [&](auto stage, auto pslot) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int PS = decltype(pslot)::value;
+    const int r0 = cur_t * kTileRows;
+    if (++cur_t == n_qt) cur_t = t_first;
+    // entry i is query row r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
+    float lse[16], pv[16];
+    read_rows16(reinterpret_cast<const float*>(smem + rows_rd + ST * 2048), 0, lse);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = fmaf(xacc[i], p.c, lse[i] * -kLog2e);
+    if ((r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31)) {
+      // the entry is visible when lo <= off_i <= hi (no row of a key past the end is)
+      const int rbase = r0 + 4 * half;
+      const int hi = slen - 1 - rbase;
+      const int lo = key < slen ? (CAUSAL ? key - rbase : -kTileRows) : kTileRows;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        pv[i] = (off >= lo && off <= hi) ? pv[i] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(pv[i]);
+    unsigned char* slot = pbuf + PS * kPslot;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4*>(slot + g * 1024) =
+          f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
+  };
+  // dK wave's V phase for the tile in stage ST (P slot PS): dS = P (dP - D), rounded into pb.
+  auto phase_v_dk = [&](auto stage, auto pslot) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int PS = decltype(pslot)::value;
+    float del[16];
+    read_rows16(reinterpret_cast<const float*>(smem + rows_rd + ST * 2048 + 1024), 0, del);
+    const unsigned char* slot = pbuf + PS * kPslot;
+    float ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(slot + g * 1024);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (xacc[4 * g + r] - del[4 * g + r]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
+  };
+
+  // Slots A_t and B_t with ST = t % kRing. Tile t + kAhead is issued in A_t into the stage of
+  // tile t - 2, whose last reader (the dK wave's Q^T in B_{t-1}) finished before B_{t-1}'s
+  // closing barrier; B_t's closing barrier waits for tile t + 2, which A_{t+1} reads. The loop
+  // runs t = 0 .. n_steps: the dV wave's work ends with dV(n_steps - 1) in A_{n_steps - 1}, the
+  // dK wave's with dK(n_steps - 1) in B_{n_steps}. Both waves run every barrier.
+  auto step = [&](auto stage, auto role_c, int t) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr bool DK = decltype(role_c)::value;
+    constexpr int S1 = (ST + 1) % kRing, SM1 = (ST + kRing - 1) % kRing;
+    if (t + kAhead < n_steps) issue(Int<(ST + kAhead) % kRing>{});
+    if constexpr (!DK) {
+      if (t < n_steps) phase_m(role_c, Int<S1 * G::kTileBytes>{}, Int<ST * G::kTileBytes>{});
+    } else {
+      phase_v_dk(Int<SM1>{}, Int<SM1 % 2>{});
+    }
+    phase_sync();
+    if constexpr (!DK) {
+      phase_v_dv(Int<S1>{}, Int<S1 % 2>{});
+    } else {
+      phase_m(role_c, Int<ST * G::kTileBytes>{}, Int<SM1 * G::kTileBytes>{});
+    }
+    if (t + 2 < n_steps) dma_wait(min(kAhead - 2, n_steps - 3 - t));
+    phase_sync();
+  };
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    for (int t = 0; t <= n_steps; t += kRing) {
+      step(Int<0>{}, role_c, t);
+      if (t + 1 <= n_steps) step(Int<1>{}, role_c, t + 1);
+      if (t + 2 <= n_steps) step(Int<2>{}, role_c, t + 2);
+      if (t + 3 <= n_steps) step(Int<3>{}, role_c, t + 3);
+      if (t + 4 <= n_steps) step(Int<4>{}, role_c, t + 4);
+      if (t + 5 <= n_steps) step(Int<5>{}, role_c, t + 5);
+    }
+  };
+
+  if (n_steps > 0) {
+    {
+      // Stage kRing - 1 and P slot 1 stand in for tile -1 until tile kRing - 1 lands there:
+      // zeros, so that dS(-1) = 0 and every product with it (and with P(-1) = 0) adds 0.
+      const u32x4 zero = u32x4{0, 0, 0, 0};
+      for (int off = tid * 16; off < G::kTileBytes; off += kThreads8 * 16) {
+        *reinterpret_cast<u32x4*>(smem + kQ + (kRing - 1) * G::kTileBytes + off) = zero;
+        *reinterpret_cast<u32x4*>(smem + kDo + (kRing - 1) * G::kTileBytes + off) = zero;
+      }
+      for (int off = tid * 16; off < kPslot; off += kThreads8 * 16)
+        *reinterpret_cast<u32x4*>(smem + kPbuf + kPslot + off) = zero;
+      if (tid < 128)
+        *reinterpret_cast<u32x4*>(smem + kRows + (kRing - 1) * 2048 + tid * 16) = zero;
+    }
+    issue(Int<0>{});
+    if (n_steps > 1) issue(Int<1>{});
+    if (n_steps > 2) issue(Int<2>{});
+    if (n_steps > 3) issue(Int<3>{});
+    static_assert(kAhead == 4, "prologue issues tiles 0 .. kAhead - 1");
+    dma_wait(min(n_steps - 1, 2));  // tile 0 (with three later tiles, tile 1 too)
+    // The resident operand is complete from here on: passing it through an empty asm makes the
+    // compiler's own load tracking agree, so that it adds no memory waits inside the loop (where
+    // they would also wait for the tiles in flight).
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : "+v"(rf[s]));
+    __syncthreads();
+    // slot B_{-1}: the dV wave forms S(0) and P(0)
+    if (role == 0) {
+      phase_m(std::false_type{}, Int<0>{}, Int<(kRing - 1) * G::kTileBytes>{});
+      phase_v_dv(Int<0>{}, Int<0>{});
+    }
+    if (n_steps > 1) dma_wait(min(kAhead - 2, n_steps - 2));  // tile 1
+    phase_sync();
+    if (role)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
+  if (key < slen) {
+    if (role)
+      store_rows<D, BF16>(p.dk + bidx * p.dk_sb + hk * p.dk_sh + int64_t(seq0 + key) * p.dk_sn,
+                          acc, p.scale, half);
+    else
+      store_rows<D, BF16>(p.dv + bidx * p.dv_sb + hk * p.dv_sh + int64_t(seq0 + key) * p.dv_sn,
+                          acc, 1.f, half);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
