@@ -226,16 +226,17 @@ __device__ __forceinline__ void tile_sync() {
 // each, waves 4-7 dK for the same keys; a SIMD holds one of each, and the two alternate, one
 // barrier-delimited phase apart, between matrix work (M phase) and element-wise work (V
 // phase), so that each SIMD overlaps one wave's exponentials or products with the other's
-// MFMAs. For query tile t (32 rows of one query head; the tiles of every query head that
-// shares the kv head follow each other):
-//   slot A_t: dV wave M: S(t+1) = Q(t+1) K^T interleaved with dV^T += dO(t)^T P(t);
+// MFMAs. Query tiles of 64 rows (of one query head; the tiles of every query head that
+// shares the kv head follow each other) are processed as two 32-row halves. For tile t:
+//   slot A_t: dV wave M: S(t) = Q(t) K^T interleaved with dV^T += dO(t-1)^T P(t-1);
 //             dK wave V: dS(t-1) = P(t-1) (dP(t-1) - D(t-1)), rounded as the B operand;
-//   slot B_t: dV wave V: P(t+1) = exp2(c S(t+1) - log2(e) L) (masked), stored in fp32 for the
-//             dK wave (two LDS slots by tile parity) and rounded as its own B operand;
+//   slot B_t: dV wave V: P(t) = exp2(c S(t) - log2(e) L) (masked), stored in fp32 for the dK
+//             wave and rounded as its own B operand;
 //             dK wave M: dP(t) = dO(t) V^T interleaved with dK^T += Q(t-1)^T dS(t-1).
-// Q and dO tiles, with the tile's L and D, stream through a six-stage LDS ring by direct-to-LDS
-// loads issued four tiles ahead; each is stored once, in the swizzled layout that serves both
-// its operand and its transposing reads.
+// P(t) is written in B_t and read in A_{t+1}, so one LDS slot holds it. Q and dO tiles, with
+// the tile's L and D, stream through a three-stage LDS ring by direct-to-LDS loads issued one
+// tile ahead; each is stored once, in the swizzled layout that serves both its operand and its
+// transposing reads.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -244,17 +245,18 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  constexpr int kPer = G::kBlocks / 4;  // 1 KB blocks of its tensor a wave loads per tile
-  // Ring stage x of each tensor: Q tile at kQ + x kTileBytes, dO tile at kDo + x kTileBytes,
-  // 32 LSE at kRows + 2048 x and 32 D 1 KB after them (each a 1 KB direct-to-LDS load); each
-  // region spans less than 64 KB, so a per-lane base plus an immediate reaches every stage.
-  constexpr int kRing = 6;
-  constexpr int kAhead = 4;  // tiles issued ahead of the one whose slot A starts
-  constexpr int kQ = 0, kDo = kRing * G::kTileBytes, kRows = 2 * kRing * G::kTileBytes;
-  constexpr int kPbuf = kRows + kRing * 2048;  // P of each key group: two slots of 4 x 16 fp32/lane
-  constexpr int kPslot = 4 * 4096;
-  static_assert(kRing % 2 == 0 && kRing >= kAhead + 2, "ring stages");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPbuf + 2 * kPslot];
+  constexpr int kRowsT = 2 * kTileRows;        // query rows per tile
+  constexpr int kHalfBytes = G::kTileBytes;    // one 32-row half of a tile
+  constexpr int kTBytes = 2 * G::kTileBytes;   // a 64-row tile of one tensor
+  constexpr int kPer = 2 * G::kBlocks / 4;     // 1 KB blocks of its tensor a wave loads per tile
+  constexpr int kRing = 3;
+  // Ring stage x of each tensor: Q tile at kQ + x kTBytes, dO tile at kDo + x kTBytes, 64 LSE
+  // at kRows + 2048 x and 64 D 1 KB after them (each a 1 KB direct-to-LDS load); each region
+  // spans less than 64 KB, so a per-lane base plus an immediate reaches every stage.
+  constexpr int kQ = 0, kDo = kRing * kTBytes, kRows = 2 * kRing * kTBytes;
+  constexpr int kPbuf = kRows + kRing * 2048;  // P of each key group: 64 rows x 32 keys fp32
+  constexpr int kPwave = 2 * 4096;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPbuf + 4 * kPwave];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -277,69 +279,52 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   const int kw0 = k0 + 32 * (wave & 3);  // first key of this wave
   const int key = kw0 + (lane & 31);     // key of this lane (accumulator column)
 
-  const int t_first = CAUSAL ? k0 / kTileRows : 0;
-  const int n_qt = (slen + kTileRows - 1) / kTileRows;
+  const int t_first = CAUSAL ? k0 / kRowsT : 0;
+  const int n_qt = (slen + kRowsT - 1) / kRowsT;
   const int per_head = n_qt - t_first;
   const int n_steps = per_head * p.group;
 
-  // DMA: waves 0-3 load the Q blocks of a tile, waves 4-7 the dO blocks, kPer each; waves 0
-  // and 1 also load the tile's 32 LSE and 32 D values (lanes 0..7 carry them, the rest read 0).
+  // DMA: waves 0-3 load the Q blocks of a tile, waves 4-7 the dO blocks, kPer each (block b is
+  // block b % kSteps of half b / kSteps); waves 0 and 1 also load the tile's 64 LSE and 64 D
+  // values (lanes 0..15 carry them, the rest read 0).
   const bool is_do = role;
   const int64_t lay_sn = is_do ? p.do_sn : p.q_sn;
   const int64_t lay_sh = is_do ? p.do_sh : p.q_sh;
   int ld_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
+    const int b = (wave & 3) * kPer + i;
     int row, col;
-    SwizzledTile::row_col((wave & 3) * kPer + i, lane, row, col);
-    ld_off[i] = int(row * lay_sn * 2) + col * 2;
+    SwizzledTile::row_col(b % kSteps, lane, row, col);
+    ld_off[i] = int((row + kTileRows * (b / kSteps)) * lay_sn * 2) + col * 2;
   }
   // The next tile to issue, carried from tile to tile (tile x is query tile t_first +
   // x % per_head of query head it.h * group + x / per_head): its tile index, row pointer and
   // LSE/D row; a change of head adds the jump to the next head's first tile.
   const int hq0 = it.h * p.group;
   const uint16_t* iss_src = (is_do ? p.dout + bidx * p.do_sb : p.q + bidx * p.q_sb) +
-                            hq0 * lay_sh + int64_t(seq0 + t_first * kTileRows) * lay_sn;
-  const int64_t src_step = int64_t(kTileRows) * lay_sn;
+                            hq0 * lay_sh + int64_t(seq0 + t_first * kRowsT) * lay_sn;
+  const int64_t src_step = int64_t(kRowsT) * lay_sn;
   const int64_t src_jump = lay_sh - int64_t(per_head) * src_step;
-  int64_t iss_lrow = (int64_t(bidx) * p.heads_q + hq0) * p.seqlen + seq0 + t_first * kTileRows;
-  const int64_t lrow_jump = p.seqlen - int64_t(per_head) * kTileRows;
+  int64_t iss_lrow = (int64_t(bidx) * p.heads_q + hq0) * p.seqlen + seq0 + t_first * kRowsT;
+  const int64_t lrow_jump = p.seqlen - int64_t(per_head) * kRowsT;
   int iss_t = t_first;
-  auto issue = [&](auto stage) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    const int rows = min(slen - iss_t * kTileRows, kTileRows);
+  auto issue = [&](int stage) __attribute__((always_inline)) {
+    const int rows = min(slen - iss_t * kRowsT, kRowsT);
     const u32x4 rs = make_rsrc(iss_src, int((rows - 1) * lay_sn * 2) + D * 2);
-    const uint32_t base = lds0 + (is_do ? kDo : kQ) + ST * G::kTileBytes + (wave & 3) * kPer * 1024;
+    const uint32_t base = lds0 + (is_do ? kDo : kQ) + stage * kTBytes + (wave & 3) * kPer * 1024;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     if (wave < 2) {
       const float* lsrc = wave == 0 ? p.lse + iss_lrow : p.delta + iss_lrow;
-      dma16(make_rsrc(lsrc, rows * 4), lds0 + kRows + ST * 2048 + wave * 1024, lane * 16);
+      dma16(make_rsrc(lsrc, rows * 4), lds0 + kRows + stage * 2048 + wave * 1024, lane * 16);
     }
     iss_src += src_step;
-    iss_lrow += kTileRows;
+    iss_lrow += kRowsT;
     if (++iss_t == n_qt) {
       iss_t = t_first;
       iss_src += src_jump;
       iss_lrow += lrow_jump;
-    }
-  };
-  // wait until this wave's loads of a tile are in LDS, `after` of its tiles issued later
-  auto dma_wait = [&](int after) __attribute__((always_inline)) {
-    if (wave < 2) {
-      if (after >= 2)
-        wait_vmcnt<2 * (kPer + 1)>();
-      else if (after == 1)
-        wait_vmcnt<kPer + 1>();
-      else
-        wait_vmcnt<0>();
-    } else {
-      if (after >= 2)
-        wait_vmcnt<2 * kPer>();
-      else if (after == 1)
-        wait_vmcnt<kPer>();
-      else
-        wait_vmcnt<0>();
     }
   };
   // phase boundary: a workgroup barrier that orders the P hand-off through LDS (a fence on
@@ -350,7 +335,6 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // per-lane LDS read offsets of the swizzled tiles
   // per-lane LDS read offsets, each with its region's start folded in and hidden from the
   // compiler, so that it addresses every stage of a region as this base plus an immediate
   // instead of keeping one address register per stage
@@ -367,9 +351,9 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   const int do_tr0 = lane_base(kDo + SwizzledTile::transpose_offset(lane, 0));
   const int do_tr1 = lane_base(kDo + SwizzledTile::transpose_offset(lane, 1));
   const int rows_rd = lane_base(kRows + 16 * half);
-  // P hand-off, slot x % 2 for tile x: entries 4 g .. 4 g + 3 of lane L at 1 KB block g,
-  // byte 16 L, of the wave's 4 KB
-  unsigned char* const pbuf = smem + lane_base(kPbuf + (wave & 3) * 4096 + lane * 16);
+  // P hand-off: entries 4 g .. 4 g + 3 of half hf, lane L at byte 4096 hf + 1024 g + 16 L of
+  // the wave's 8 KB
+  unsigned char* const pbuf = smem + lane_base(kPbuf + (wave & 3) * kPwave + lane * 16);
 
   // resident B operand: K^T (sign of the scale applied) for the dV wave, V^T for the dK wave
   u32x4 rf[kSteps];
@@ -385,42 +369,50 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   f32x16 acc[kOBlocks];  // dV^T or dK^T: lane holds head-dims of its key column
 #pragma unroll
   for (int j = 0; j < kOBlocks; ++j) acc[j] = f32x16{};
-  f32x16 xacc = f32x16{};  // S (dV wave) or dP (dK wave) of the tile between its two phases
-  u32x4 pb[2];             // P (dV wave) or dS (dK wave), rounded: B operand of the row chain
-  pb[0] = pb[1] = u32x4{0, 0, 0, 0};
+  f32x16 xacc[2];  // S (dV wave) or dP (dK wave) of each half of the tile between its phases
+  xacc[0] = xacc[1] = f32x16{};
+  u32x4 pb[4];     // P (dV wave) or dS (dK wave), rounded: B operands of the row chain
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pb[u] = u32x4{0, 0, 0, 0};
 
-  // M phase: the chain over head-dims (xacc = tile rows of `xsrc` (operand reads) . rf) and
-  // the chain over rows (acc[j] += (head-dims of block j of `ysrc`, transposing reads) . pb),
-  // interleaved one to one, each LDS operand read kAheadM MFMAs before its MFMA.
-  constexpr int kMfma = 2 * kSteps;
+  // M phase: the chains over head-dims of the two halves (xacc[hf] = rows of half hf of the
+  // tile in stage xs (operand reads) . rf) and the chain over rows (acc[j] += (head-dims of
+  // block j of the tile in stage ys, transposing reads) . pb), interleaved one to one, each
+  // LDS operand read kAheadM MFMAs before its MFMA.
+  constexpr int kMfma = 4 * kSteps;
+  static_assert(4 * kOBlocks == 2 * kSteps, "one row-chain MFMA per d-chain MFMA");
   constexpr int kAheadM = 8;
-  auto phase_m = [&](auto dk_c, auto xoff, auto yoff) __attribute__((always_inline)) {
+  auto phase_m = [&](auto dk_c, int xs, int ys) __attribute__((always_inline)) {
     constexpr bool DK = decltype(dk_c)::value;  // d chain over dO, row chain over Q
-    constexpr int XO = decltype(xoff)::value;  // stage offset of the tile read by the d chain
-    constexpr int YO = decltype(yoff)::value;  // stage offset of the tile read by the row chain
-    const int x0 = DK ? do_op0 : q_op0, x1 = DK ? do_op1 : q_op1;
-    const int y0 = DK ? q_tr0 : do_tr0, y1 = DK ? q_tr1 : do_tr1;
+    const int x0 = (DK ? do_op0 : q_op0) + xs * kTBytes;
+    const int x1 = (DK ? do_op1 : q_op1) + xs * kTBytes;
+    const int y0 = (DK ? q_tr0 : do_tr0) + ys * kTBytes;
+    const int y1 = (DK ? q_tr1 : do_tr1) + ys * kTBytes;
     u32x4 opnd[kMfma];
+    // MFMA n: even n is d-chain step s = n / 4 of half (n / 2) % 2; odd n is row-chain MFMA
+    // m = n / 2, head-dim block m % kOBlocks, 16-row step u = m / kOBlocks (half u / 2)
     auto fetch = [&](auto nn) __attribute__((always_inline)) {
       constexpr int n = decltype(nn)::value;
       if constexpr (n % 2 == 0) {
-        constexpr int s = n / 2;
-        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? x1 : x0) + XO + s * 1024);
+        constexpr int hf = (n / 2) % 2, s = n / 4;
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? x1 : x0) + hf * kHalfBytes +
+                                                  s * 1024);
       } else {
-        constexpr int m = n / 2, j = m % kOBlocks, tt = m / kOBlocks;
-        const u32x2 lo = E::read_tr(smem + y0 + YO + 2048 * j + 256 * tt);
-        const u32x2 hi = E::read_tr(smem + y1 + YO + 2048 * j + 256 * tt);
+        constexpr int m = n / 2, j = m % kOBlocks, u = m / kOBlocks;
+        constexpr int off = (u / 2) * kHalfBytes + 2048 * j + 256 * (u % 2);
+        const u32x2 lo = E::read_tr(smem + y0 + off);
+        const u32x2 hi = E::read_tr(smem + y1 + off);
         opnd[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     };
     auto mfma = [&](auto nn) __attribute__((always_inline)) {
       constexpr int n = decltype(nn)::value;
       if constexpr (n % 2 == 0) {
-        constexpr int s = n / 2;
-        xacc = E::mfma(opnd[n], rf[s], s == 0 ? f32x16{} : xacc);
+        constexpr int hf = (n / 2) % 2, s = n / 4;
+        xacc[hf] = E::mfma(opnd[n], rf[s], s == 0 ? f32x16{} : xacc[hf]);
       } else {
-        constexpr int m = n / 2, j = m % kOBlocks, tt = m / kOBlocks;
-        acc[j] = E::mfma(opnd[n], pb[tt], acc[j]);
+        constexpr int m = n / 2, j = m % kOBlocks, u = m / kOBlocks;
+        acc[j] = E::mfma(opnd[n], pb[u], acc[j]);
       }
     };
     [&]<int... n>(std::integer_sequence<int, n...>) {
@@ -437,131 +429,119 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     }(std::make_integer_sequence<int, kMfma>{});
   };
 
-  // dV wave's V phase for the tile in stage ST (P slot PS): P = exp2(c S - log2(e) L), masked
-  // where the key is past the end or above the diagonal; stored for the dK wave, rounded into pb.
+  // dV wave's V phase for the tile in stage `stage`: P = exp2(c S - log2(e) L), masked where
+  // the key is past the end or above the diagonal; stored for the dK wave, rounded into pb.
   int cur_t = t_first;  // query tile of the next V phase (advanced like the issue's)
-  auto phase_v_dv = [&](auto stage, auto pslot) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    constexpr int PS = decltype(pslot)::value;
-    const int r0 = cur_t * kTileRows;
+  auto phase_v_dv = [&](int stage) __attribute__((always_inline)) {
+    const int r0t = cur_t * kRowsT;
     if (++cur_t == n_qt) cur_t = t_first;
-    // entry i is query row r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
-    float lse[16], pv[16];
-    read_rows16(reinterpret_cast<const float*>(smem + rows_rd + ST * 2048), 0, lse);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] = fmaf(xacc[i], p.c, lse[i] * -kLog2e);
-    if ((r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31)) {
-      // the entry is visible when lo <= off_i <= hi (no row of a key past the end is)
-      const int rbase = r0 + 4 * half;
-      const int hi = slen - 1 - rbase;
-      const int lo = key < slen ? (CAUSAL ? key - rbase : -kTileRows) : kTileRows;
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r0 = r0t + kTileRows * hf;
+      // entry i is query row r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
+      float lse[16], pv[16];
+      read_rows16(reinterpret_cast<const float*>(smem + rows_rd + stage * 2048 + 128 * hf), 0,
+                  lse);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = 8 * (i >> 2) + (i & 3);
-        pv[i] = (off >= lo && off <= hi) ? pv[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) pv[i] = fmaf(xacc[hf][i], p.c, lse[i] * -kLog2e);
+      if ((r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31)) {
+        // the entry is visible when lo <= off_i <= hi (no row of a key past the end is)
+        const int rbase = r0 + 4 * half;
+        const int hi = slen - 1 - rbase;
+        const int lo = key < slen ? (CAUSAL ? key - rbase : -kTileRows) : kTileRows;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 8 * (i >> 2) + (i & 3);
+          pv[i] = (off >= lo && off <= hi) ? pv[i] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(pv[i]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(pbuf + 4096 * hf + g * 1024) =
+            f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[2 * hf + tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(pv[i]);
-    unsigned char* slot = pbuf + PS * kPslot;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<f32x4*>(slot + g * 1024) =
-          f32x4{pv[4 * g], pv[4 * g + 1], pv[4 * g + 2], pv[4 * g + 3]};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pb[tt][w] = E::pack(pv[8 * tt + 2 * w], pv[8 * tt + 2 * w + 1]);
   };
-  // dK wave's V phase for the tile in stage ST (P slot PS): dS = P (dP - D), rounded into pb.
-  auto phase_v_dk = [&](auto stage, auto pslot) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    constexpr int PS = decltype(pslot)::value;
-    float del[16];
-    read_rows16(reinterpret_cast<const float*>(smem + rows_rd + ST * 2048 + 1024), 0, del);
-    const unsigned char* slot = pbuf + PS * kPslot;
-    float ds[16];
+  // dK wave's V phase for the tile in stage `stage`: dS = P (dP - D), rounded into pb.
+  auto phase_v_dk = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(slot + g * 1024);
+    for (int hf = 0; hf < 2; ++hf) {
+      float del[16];
+      read_rows16(reinterpret_cast<const float*>(smem + rows_rd + stage * 2048 + 1024 + 128 * hf),
+                  0, del);
+      float ds[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ds[4 * g + r] = pv[r] * (xacc[4 * g + r] - del[4 * g + r]);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(pbuf + 4096 * hf + g * 1024);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ds[4 * g + r] = pv[r] * (xacc[hf][4 * g + r] - del[4 * g + r]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          pb[2 * hf + tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
     }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pb[tt][w] = E::pack(ds[8 * tt + 2 * w], ds[8 * tt + 2 * w + 1]);
   };
 
-  // Slots A_t and B_t with ST = t % kRing. Tile t + kAhead is issued in A_t into the stage of
-  // tile t - 2, whose last reader (the dK wave's Q^T in B_{t-1}) finished before B_{t-1}'s
-  // closing barrier; B_t's closing barrier waits for tile t + 2, which A_{t+1} reads. The loop
-  // runs t = 0 .. n_steps: the dV wave's work ends with dV(n_steps - 1) in A_{n_steps - 1}, the
-  // dK wave's with dK(n_steps - 1) in B_{n_steps}. Both waves run every barrier.
-  auto step = [&](auto stage, auto role_c, int t) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    constexpr bool DK = decltype(role_c)::value;
-    constexpr int S1 = (ST + 1) % kRing, SM1 = (ST + kRing - 1) % kRing;
-    if (t + kAhead < n_steps) issue(Int<(ST + kAhead) % kRing>{});
-    if constexpr (!DK) {
-      if (t < n_steps) phase_m(role_c, Int<S1 * G::kTileBytes>{}, Int<ST * G::kTileBytes>{});
-    } else {
-      phase_v_dk(Int<SM1>{}, Int<SM1 % 2>{});
-    }
-    phase_sync();
-    if constexpr (!DK) {
-      phase_v_dv(Int<S1>{}, Int<S1 % 2>{});
-    } else {
-      phase_m(role_c, Int<ST * G::kTileBytes>{}, Int<SM1 * G::kTileBytes>{});
-    }
-    if (t + 2 < n_steps) dma_wait(min(kAhead - 2, n_steps - 3 - t));
-    phase_sync();
-  };
+  // Slots A_t and B_t, with the ring stage of tile t a loop variable. Tile t + 1 is issued in
+  // A_t into the stage of tile t - 2, whose last reader (the dK wave's Q^T in B_{t-1}) finished
+  // before B_{t-1}'s closing barrier; B_t's closing barrier waits for it (A_{t+1} reads it).
+  // The loop runs t = 0 .. n_steps, every phase unconditional: in A_0 and B_0 the products
+  // with tile -1 meet zeros (stage kRing - 1, P and the B operands start at 0); in A_{n_steps}
+  // and B_{n_steps} the d chains read a stale stage and their results, like P(n_steps), are
+  // never used. Both waves run every barrier.
   auto run = [&](auto role_c) __attribute__((always_inline)) {
-    for (int t = 0; t <= n_steps; t += kRing) {
-      step(Int<0>{}, role_c, t);
-      if (t + 1 <= n_steps) step(Int<1>{}, role_c, t + 1);
-      if (t + 2 <= n_steps) step(Int<2>{}, role_c, t + 2);
-      if (t + 3 <= n_steps) step(Int<3>{}, role_c, t + 3);
-      if (t + 4 <= n_steps) step(Int<4>{}, role_c, t + 4);
-      if (t + 5 <= n_steps) step(Int<5>{}, role_c, t + 5);
+    constexpr bool DK = decltype(role_c)::value;
+    int st = 0, st_prev = kRing - 1, st_next = 1;
+    for (int t = 0; t <= n_steps; ++t) {
+      if (t + 1 < n_steps) issue(st_next);
+      if constexpr (!DK)
+        phase_m(role_c, st, st_prev);
+      else
+        phase_v_dk(st_prev);
+      phase_sync();
+      if constexpr (!DK)
+        phase_v_dv(st);
+      else
+        phase_m(role_c, st, st_prev);
+      if (t + 1 < n_steps) wait_vmcnt<0>();  // tile t + 1
+      phase_sync();
+      st_prev = st;
+      st = st_next;
+      st_next = st_next == kRing - 1 ? 0 : st_next + 1;
     }
   };
 
   if (n_steps > 0) {
     {
-      // Stage kRing - 1 and P slot 1 stand in for tile -1 until tile kRing - 1 lands there:
-      // zeros, so that dS(-1) = 0 and every product with it (and with P(-1) = 0) adds 0.
+      // Stage kRing - 1 (Q, dO, L and D) and P stand in for tile -1 until tile kRing - 1 lands
+      // there: zeros, so that dS(-1) = 0 and every product with tile -1 adds 0.
       const u32x4 zero = u32x4{0, 0, 0, 0};
-      for (int off = tid * 16; off < G::kTileBytes; off += kThreads8 * 16) {
-        *reinterpret_cast<u32x4*>(smem + kQ + (kRing - 1) * G::kTileBytes + off) = zero;
-        *reinterpret_cast<u32x4*>(smem + kDo + (kRing - 1) * G::kTileBytes + off) = zero;
+      for (int off = tid * 16; off < kTBytes; off += kThreads8 * 16) {
+        *reinterpret_cast<u32x4*>(smem + kQ + (kRing - 1) * kTBytes + off) = zero;
+        *reinterpret_cast<u32x4*>(smem + kDo + (kRing - 1) * kTBytes + off) = zero;
       }
-      for (int off = tid * 16; off < kPslot; off += kThreads8 * 16)
-        *reinterpret_cast<u32x4*>(smem + kPbuf + kPslot + off) = zero;
+      for (int off = tid * 16; off < 4 * kPwave; off += kThreads8 * 16)
+        *reinterpret_cast<u32x4*>(smem + kPbuf + off) = zero;
       if (tid < 128)
         *reinterpret_cast<u32x4*>(smem + kRows + (kRing - 1) * 2048 + tid * 16) = zero;
     }
-    issue(Int<0>{});
-    if (n_steps > 1) issue(Int<1>{});
-    if (n_steps > 2) issue(Int<2>{});
-    if (n_steps > 3) issue(Int<3>{});
-    static_assert(kAhead == 4, "prologue issues tiles 0 .. kAhead - 1");
-    dma_wait(min(n_steps - 1, 2));  // tile 0 (with three later tiles, tile 1 too)
-    // The resident operand is complete from here on: passing it through an empty asm makes the
-    // compiler's own load tracking agree, so that it adds no memory waits inside the loop (where
-    // they would also wait for the tiles in flight).
+    issue(0);
+    // Tile 0 and the resident operand are complete from here on: passing the operand through
+    // an empty asm makes the compiler's own load tracking agree, so that it adds no memory
+    // waits inside the loop (where they would also wait for the tile in flight).
     wait_vmcnt<0>();
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) asm volatile("" : "+v"(rf[s]));
     __syncthreads();
-    // slot B_{-1}: the dV wave forms S(0) and P(0)
-    if (role == 0) {
-      phase_m(std::false_type{}, Int<0>{}, Int<(kRing - 1) * G::kTileBytes>{});
-      phase_v_dv(Int<0>{}, Int<0>{});
-    }
-    if (n_steps > 1) dma_wait(min(kAhead - 2, n_steps - 2));  // tile 1
-    phase_sync();
     if (role)
       run(std::true_type{});
     else
@@ -578,7 +558,15 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// dQ: one workgroup per 256 queries, 8 waves of 32 queries.
+// dQ: one workgroup per 256 queries, 8 waves of 32 queries, Q^T and dO^T resident and dQ^T
+// accumulating in each. The waves of a SIMD (w and w + 4, groups 0 and 1) alternate, one
+// barrier-delimited phase apart, between an M phase, M(t): S^T(t) = K(t) Q^T and
+// dP^T(t) = V(t) dO^T interleaved with dQ^T += K(t-1)^T dS^T(t-1), and a V phase, V(t):
+// dS^T(t) = P^T(t) (dP^T(t) - D) with P^T(t) = exp2(c S^T(t) - log2(e) L) (masked), rounded
+// as the next M phase's B operand. Slot 2t: group 0 runs M(t), group 1 V(t-1); slot 2t+1:
+// group 0 runs V(t), group 1 M(t). 32-key tiles of K and V stream through a six-stage LDS
+// ring by direct-to-LDS loads issued four tiles ahead; each is stored once, in the swizzled
+// layout (K serves both its operand and its transposing reads).
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -587,16 +575,19 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  // stage: K operand | V operand | K transposing
-  constexpr int kKop = 0, kVop = G::kTileBytes, kKtr = 2 * G::kTileBytes;
-  constexpr int kStage = 3 * G::kTileBytes;
-  constexpr int kDmaBlocks = 3 * G::kBlocks;  // per tile, spread over the 8 waves
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+  constexpr int kPer = G::kBlocks / 4;  // 1 KB blocks of its tensor a wave loads per tile
+  constexpr int kRing = 6;
+  constexpr int kAhead = 4;  // tiles issued ahead of the one whose slot 2t starts
+  // ring stage x: K tile at kK + x kTileBytes, V tile at kV + x kTileBytes
+  constexpr int kK = 0, kV = kRing * G::kTileBytes;
+  static_assert(kRing % 2 == 0 && kRing >= kAhead + 2, "ring stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kRing * G::kTileBytes];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int half = lane >> 5;
 
   const int pairs = gridDim.x / p.n_qblocks;
@@ -611,16 +602,16 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   }
   const int q0 = it.blk * 256;
   if (q0 >= slen) return;  // uniform across the workgroup
-  const int qw0 = q0 + 32 * wave;      // first query of this wave
-  const int qrow = qw0 + (lane & 31);  // query of this lane (accumulator column)
+  // The waves of a SIMD take neighbouring 32-query slices, so both reach the causal diagonal
+  // at nearly the same tile.
+  const int qw0 = q0 + 32 * (2 * (wave & 3) + grp);  // first query of this wave
+  const int qrow = qw0 + (lane & 31);                 // query of this lane (accumulator column)
 
   u32x4 qf[kSteps], dof[kSteps];
   load_resident<D>(p.q + bidx * p.q_sb + h * p.q_sh + int64_t(seq0) * p.q_sn, p.q_sn, qw0, slen,
                    lane, qf);
   load_resident<D>(p.dout + bidx * p.do_sb + h * p.do_sh + int64_t(seq0) * p.do_sn, p.do_sn, qw0,
                    slen, lane, dof);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) qf[s] = (qf[s] & p.s_and) ^ p.s_xor;
   float nlse = 0.f, del = 0.f;  // -log2e LSE and D of this lane's query
   if (qrow < slen) {
     const int64_t r = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + qrow;
@@ -634,85 +625,190 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   const int kv_end = CAUSAL ? min(slen, q0 + 256) : slen;
   const int n_tiles = (kv_end + kTileRows - 1) / kTileRows;
 
-  // DMA: block b of the tile's three layouts (K op, V op, K tr) goes to wave b % 8
-  constexpr int kPerW = (kDmaBlocks + kWaves - 1) / kWaves;
-  int ld_off[kPerW];
+  // DMA: waves 0-3 load the K blocks of a tile, waves 4-7 the V blocks, kPer each
+  const int64_t lay_sn = grp ? p.v_sn : p.k_sn;
+  int ld_off[kPer];
 #pragma unroll
-  for (int i = 0; i < kPerW; ++i) {
-    const int b = i * kWaves + wave;
-    const int lay = b / G::kBlocks, blk = b % G::kBlocks;
-    int row = 0, col = 0;
-    if (lay < 2)
-      OperandLayout::row_col(blk, lane, kSteps, row, col);
-    else
-      TransposeLayout::row_col(blk, lane, kOBlocks, row, col);
-    ld_off[i] = int(row * (lay == 1 ? p.v_sn : p.k_sn) * 2) + col * 2;
+  for (int i = 0; i < kPer; ++i) {
+    int row, col;
+    SwizzledTile::row_col((wave & 3) * kPer + i, lane, row, col);
+    ld_off[i] = int(row * lay_sn * 2) + col * 2;
   }
-  // K and V rows of the next tile to issue, carried from tile to tile
-  const uint16_t* kcur = p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
-  const uint16_t* vcur = p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn;
+  // rows of the next tile to issue, carried from tile to tile
+  const uint16_t* iss_src = grp ? p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn
+                                : p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
+  const int64_t src_step = int64_t(kTileRows) * lay_sn;
   int iss_r0 = 0;
-  auto issue = [&](auto stage) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
+  auto issue = [&](int stage) __attribute__((always_inline)) {
     const int rows = min(slen - iss_r0, kTileRows);
-    const u32x4 rk = make_rsrc(kcur, int((rows - 1) * p.k_sn * 2) + D * 2);
-    const u32x4 rv = make_rsrc(vcur, int((rows - 1) * p.v_sn * 2) + D * 2);
-    kcur += int64_t(kTileRows) * p.k_sn;
-    vcur += int64_t(kTileRows) * p.v_sn;
-    iss_r0 += kTileRows;
+    const u32x4 rs = make_rsrc(iss_src, int((rows - 1) * lay_sn * 2) + D * 2);
+    const uint32_t base = lds0 + (grp ? kV : kK) + stage * G::kTileBytes + (wave & 3) * kPer * 1024;
 #pragma unroll
-    for (int i = 0; i < kPerW; ++i) {
-      const int b = i * kWaves + wave;
-      if (b < kDmaBlocks) {
-        const int lay = b / G::kBlocks, blk = b % G::kBlocks;
-        dma16(lay == 1 ? rv : rk, lds0 + ST * kStage + lay * G::kTileBytes + blk * 1024,
-              ld_off[i]);
-      }
-    }
+    for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
+    iss_src += src_step;
+    iss_r0 += kTileRows;
+  };
+  // wait until this wave's loads of a tile are in LDS, `after` of its tiles issued later
+  auto dma_wait = [&](int after) __attribute__((always_inline)) {
+    if (after >= 3)
+      wait_vmcnt<3 * kPer>();
+    else if (after == 2)
+      wait_vmcnt<2 * kPer>();
+    else if (after == 1)
+      wait_vmcnt<kPer>();
+    else
+      wait_vmcnt<0>();
+  };
+  auto phase_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto compute = [&](auto stage, int tile) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage)::value;
-    const unsigned char* sb = smem + ST * kStage;
+  // per-lane LDS read offsets (region start folded in, hidden from the compiler so that every
+  // stage is this base plus an immediate)
+  auto lane_base = [](int off) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(off));
+    return off;
+  };
+  const int k_op0 = lane_base(kK + SwizzledTile::operand_offset(lane, 0));
+  const int k_op1 = lane_base(kK + SwizzledTile::operand_offset(lane, 1));
+  const int k_tr0 = lane_base(kK + SwizzledTile::transpose_offset(lane, 0));
+  const int k_tr1 = lane_base(kK + SwizzledTile::transpose_offset(lane, 1));
+  const int v_op0 = lane_base(kV + SwizzledTile::operand_offset(lane, 0));
+  const int v_op1 = lane_base(kV + SwizzledTile::operand_offset(lane, 1));
+
+  f32x16 sacc = f32x16{}, dpacc = f32x16{};  // S^T and dP^T of the tile between its phases
+  u32x4 pb[2];                               // dS^T of the previous tile, rounded (B operand)
+  pb[0] = pb[1] = u32x4{0, 0, 0, 0};
+
+  // M phase on the tile in stage XS (S^T and dP^T chains) and the previous tile in stage YS
+  // (dQ^T chain), interleaved S, dP, dQ; each LDS operand read kAheadM MFMAs before its MFMA.
+  constexpr int kMfma = 3 * kSteps;
+  static_assert(2 * kOBlocks == kSteps, "one dQ MFMA per S MFMA");
+  constexpr int kAheadM = 4;
+  auto phase_m = [&](int xs, int ys) __attribute__((always_inline)) {
+    const int xo = xs * G::kTileBytes, yo = ys * G::kTileBytes;
+    const int ko0 = k_op0 + xo, ko1 = k_op1 + xo, vo0 = v_op0 + xo, vo1 = v_op1 + xo;
+    const int kt0 = k_tr0 + yo, kt1 = k_tr1 + yo;
+    u32x4 opnd[kMfma];
+    auto fetch = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value, s = n / 3;
+      if constexpr (n % 3 == 0) {
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? ko1 : ko0) + s * 1024);
+      } else if constexpr (n % 3 == 1) {
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? vo1 : vo0) + s * 1024);
+      } else {
+        constexpr int j = s % kOBlocks, tt = s / kOBlocks;
+        const u32x2 lo = E::read_tr(smem + kt0 + 2048 * j + 256 * tt);
+        const u32x2 hi = E::read_tr(smem + kt1 + 2048 * j + 256 * tt);
+        opnd[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+    auto mfma = [&](auto nn) __attribute__((always_inline)) {
+      constexpr int n = decltype(nn)::value, s = n / 3;
+      if constexpr (n % 3 == 0) {
+        sacc = E::mfma(opnd[n], qf[s], s == 0 ? f32x16{} : sacc);
+      } else if constexpr (n % 3 == 1) {
+        dpacc = E::mfma(opnd[n], dof[s], s == 0 ? f32x16{} : dpacc);
+      } else {
+        constexpr int j = s % kOBlocks, tt = s / kOBlocks;
+        dqacc[j] = E::mfma(opnd[n], pb[tt], dqacc[j]);
+      }
+    };
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      (fetch(Int<n>{}), ...);
+    }(std::make_integer_sequence<int, kAheadM>{});
+    [&]<int... n>(std::integer_sequence<int, n...>) {
+      ((
+           [&] {
+             if constexpr (n + kAheadM < kMfma) fetch(Int<n + kAheadM>{});
+             mfma(Int<n>{});
+             __builtin_amdgcn_sched_barrier(0);
+           }()),
+       ...);
+    }(std::make_integer_sequence<int, kMfma>{});
+  };
+
+  // V phase of key tile `tile`: dS^T = P^T (dP^T - D), P^T = exp2(c S^T - log2(e) L), with
+  // P = 0 where the key is past the end or above the diagonal; rounded into pb.
+  auto phase_v = [&](int tile) __attribute__((always_inline)) {
     const int r0 = tile * kTileRows;
-    const f32x16 sacc = chain_over_d<BF16, kSteps>(sb + kKop + lane * 16, qf);
-    const f32x16 dpacc = chain_over_d<BF16, kSteps>(sb + kVop + lane * 16, dof);
-    // entry i is key r0 + 8 (i / 4) + 4 half + i % 4
-    const bool edge = (r0 + kTileRows > slen) || (CAUSAL && r0 + kTileRows - 1 > qw0);
-    u32x4 pb[2];
+    // entry i is key r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sacc[i], p.c, nlse);
+    if ((r0 + kTileRows > slen) || (CAUSAL && r0 + kTileRows - 1 > qw0)) {
+      // visible while off_i <= lim
+      const int lim = (CAUSAL ? min(slen - 1, qrow) : slen - 1) - r0 - 4 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        x[i] = off <= lim ? x[i] : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        float v2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 8 * tt + 2 * w + u;
-          float x = fmaf(sacc[i], p.c, nlse);
-          if (edge) {
-            const int kk = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool ok = kk < slen && (!CAUSAL || kk <= qrow);
-            x = ok ? x : -INFINITY;
-          }
-          v2[u] = __builtin_amdgcn_exp2f(x) * (dpacc[i] - del);
-        }
-        pb[tt][w] = E::pack(v2[0], v2[1]);
+        const int i = 8 * tt + 2 * w;
+        const float d0 = __builtin_amdgcn_exp2f(x[i]) * (dpacc[i] - del);
+        const float d1 = __builtin_amdgcn_exp2f(x[i + 1]) * (dpacc[i + 1] - del);
+        pb[tt][w] = E::pack(d0, d1);
       }
-    chain_over_rows<BF16, kOBlocks>(sb + kKtr + lane * 8, pb, dqacc);
   };
 
-  issue(Int<0>{});
-  tile_sync();
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) issue(Int<1>{});
-    compute(Int<0>{}, t);
-    tile_sync();
-    if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) issue(Int<0>{});
-      compute(Int<1>{}, t + 1);
-      tile_sync();
+  // Slot 2t issues tile t + kAhead (into the stage of tile t - 2, last read by group 1's M(t-1)
+  // in slot 2t - 1); slot 2t + 1 ends by waiting for tile t + 1, which slot 2t + 2 reads. The
+  // loop runs t = 0 .. n_tiles: group 0's M(n_tiles) and group 1's M(n_tiles) only add
+  // dQ(n_tiles - 1) (their S and dP chains read a stale stage and are not used). The ring
+  // stage is a loop variable: unrolling the loop over the stages would keep more registers
+  // live than a wave has.
+  auto run = [&](auto grp_c) __attribute__((always_inline)) {
+    constexpr bool G1 = decltype(grp_c)::value;
+    int st = 0, st_prev = kRing - 1, st_issue = kAhead;  // stages of tiles t, t - 1, t + kAhead
+    for (int t = 0; t <= n_tiles; ++t) {
+      if (t + kAhead < n_tiles) issue(st_issue);
+      if constexpr (!G1) {
+        phase_m(st, st_prev);
+      } else {
+        if (t >= 1) phase_v(t - 1);
+      }
+      phase_sync();
+      if constexpr (!G1) {
+        if (t < n_tiles) phase_v(t);
+      } else {
+        phase_m(st, st_prev);
+      }
+      if (t + 1 < n_tiles) dma_wait(min(kAhead - 1, n_tiles - 2 - t));
+      phase_sync();
+      st_prev = st;
+      st = st == kRing - 1 ? 0 : st + 1;
+      st_issue = st_issue == kRing - 1 ? 0 : st_issue + 1;
     }
+  };
+
+  {
+    // The K stage kRing - 1 stands in for tile -1 until tile kRing - 1 lands there: zeros, so
+    // that dQ^T += K(-1)^T dS^T(-1) with dS^T(-1) = 0 adds 0.
+    const u32x4 zero = u32x4{0, 0, 0, 0};
+    for (int off = tid * 16; off < G::kTileBytes; off += kThreads8 * 16)
+      *reinterpret_cast<u32x4*>(smem + kK + (kRing - 1) * G::kTileBytes + off) = zero;
   }
+  for (int x = 0; x < kAhead && x < n_tiles; ++x) issue(x);
+  // tile 0 and the resident operands complete; the empty asm makes the compiler's own load
+  // tracking agree, so that it adds no memory waits inside the loop
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    qf[s] = (qf[s] & p.s_and) ^ p.s_xor;
+    asm volatile("" : "+v"(qf[s]), "+v"(dof[s]));
+  }
+  __syncthreads();
+  if (grp)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   if (qrow < slen) {
     uint16_t* dqrow = p.dq + bidx * p.dq_sb + h * p.dq_sh + int64_t(seq0 + qrow) * p.dq_sn;
