@@ -559,14 +559,15 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 
 // ---------------------------------------------------------------------------------------
 // dQ: one workgroup per 256 queries, 8 waves of 32 queries, Q^T and dO^T resident and dQ^T
-// accumulating in each. The waves of a SIMD (w and w + 4, groups 0 and 1) alternate, one
-// barrier-delimited phase apart, between an M phase, M(t): S^T(t) = K(t) Q^T and
-// dP^T(t) = V(t) dO^T interleaved with dQ^T += K(t-1)^T dS^T(t-1), and a V phase, V(t):
-// dS^T(t) = P^T(t) (dP^T(t) - D) with P^T(t) = exp2(c S^T(t) - log2(e) L) (masked), rounded
-// as the next M phase's B operand. Slot 2t: group 0 runs M(t), group 1 V(t-1); slot 2t+1:
-// group 0 runs V(t), group 1 M(t). 32-key tiles of K and V stream through a six-stage LDS
-// ring by direct-to-LDS loads issued four tiles ahead; each is stored once, in the swizzled
-// layout (K serves both its operand and its transposing reads).
+// accumulating in each. Key tiles of 64 keys are processed as two 32-key halves. The waves of
+// a SIMD (w and w + 4, groups 0 and 1) alternate, one barrier-delimited phase apart, between
+// an M phase, M(t): S^T(t) = K(t) Q^T and dP^T(t) = V(t) dO^T interleaved with
+// dQ^T += K(t-1)^T dS^T(t-1), and a V phase, V(t): dS^T(t) = P^T(t) (dP^T(t) - D) with
+// P^T(t) = exp2(c S^T(t) - log2(e) L) (masked), rounded as the next M phase's B operand.
+// Slot 2t: group 0 runs M(t), group 1 V(t-1); slot 2t+1: group 0 runs V(t), group 1 M(t).
+// K and V tiles stream through a three-stage LDS ring by direct-to-LDS loads issued one tile
+// ahead; each is stored once, in the swizzled layout (K serves both its operand and its
+// transposing reads).
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads8, kThreads8),
                           amdgpu_waves_per_eu(2, 2)))
@@ -575,13 +576,14 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   using G = BwdGeo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kOBlocks = G::kOBlocks;
-  constexpr int kPer = G::kBlocks / 4;  // 1 KB blocks of its tensor a wave loads per tile
-  constexpr int kRing = 6;
-  constexpr int kAhead = 4;  // tiles issued ahead of the one whose slot 2t starts
-  // ring stage x: K tile at kK + x kTileBytes, V tile at kV + x kTileBytes
-  constexpr int kK = 0, kV = kRing * G::kTileBytes;
-  static_assert(kRing % 2 == 0 && kRing >= kAhead + 2, "ring stages");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kRing * G::kTileBytes];
+  constexpr int kKeysT = 2 * kTileRows;       // keys per tile
+  constexpr int kHalfBytes = G::kTileBytes;   // one 32-key half of a tile
+  constexpr int kTBytes = 2 * G::kTileBytes;  // a 64-key tile of one tensor
+  constexpr int kPer = 2 * G::kBlocks / 4;    // 1 KB blocks of its tensor a wave loads per tile
+  constexpr int kRing = 3;
+  // ring stage x: K tile at kK + x kTBytes, V tile at kV + x kTBytes
+  constexpr int kK = 0, kV = kRing * kTBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kRing * kTBytes];
   const uint32_t lds0 = lds_address(smem);
 
   const int tid = threadIdx.x;
@@ -623,41 +625,32 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   for (int j = 0; j < kOBlocks; ++j) dqacc[j] = f32x16{};
 
   const int kv_end = CAUSAL ? min(slen, q0 + 256) : slen;
-  const int n_tiles = (kv_end + kTileRows - 1) / kTileRows;
+  const int n_tiles = (kv_end + kKeysT - 1) / kKeysT;
 
-  // DMA: waves 0-3 load the K blocks of a tile, waves 4-7 the V blocks, kPer each
+  // DMA: waves 0-3 load the K blocks of a tile, waves 4-7 the V blocks, kPer each (block b is
+  // block b % kSteps of half b / kSteps)
   const int64_t lay_sn = grp ? p.v_sn : p.k_sn;
   int ld_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
+    const int b = (wave & 3) * kPer + i;
     int row, col;
-    SwizzledTile::row_col((wave & 3) * kPer + i, lane, row, col);
-    ld_off[i] = int(row * lay_sn * 2) + col * 2;
+    SwizzledTile::row_col(b % kSteps, lane, row, col);
+    ld_off[i] = int((row + kTileRows * (b / kSteps)) * lay_sn * 2) + col * 2;
   }
   // rows of the next tile to issue, carried from tile to tile
   const uint16_t* iss_src = grp ? p.v + bidx * p.v_sb + hk * p.v_sh + int64_t(seq0) * p.v_sn
                                 : p.k + bidx * p.k_sb + hk * p.k_sh + int64_t(seq0) * p.k_sn;
-  const int64_t src_step = int64_t(kTileRows) * lay_sn;
+  const int64_t src_step = int64_t(kKeysT) * lay_sn;
   int iss_r0 = 0;
   auto issue = [&](int stage) __attribute__((always_inline)) {
-    const int rows = min(slen - iss_r0, kTileRows);
+    const int rows = min(slen - iss_r0, kKeysT);
     const u32x4 rs = make_rsrc(iss_src, int((rows - 1) * lay_sn * 2) + D * 2);
-    const uint32_t base = lds0 + (grp ? kV : kK) + stage * G::kTileBytes + (wave & 3) * kPer * 1024;
+    const uint32_t base = lds0 + (grp ? kV : kK) + stage * kTBytes + (wave & 3) * kPer * 1024;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     iss_src += src_step;
-    iss_r0 += kTileRows;
-  };
-  // wait until this wave's loads of a tile are in LDS, `after` of its tiles issued later
-  auto dma_wait = [&](int after) __attribute__((always_inline)) {
-    if (after >= 3)
-      wait_vmcnt<3 * kPer>();
-    else if (after == 2)
-      wait_vmcnt<2 * kPer>();
-    else if (after == 1)
-      wait_vmcnt<kPer>();
-    else
-      wait_vmcnt<0>();
+    iss_r0 += kKeysT;
   };
   auto phase_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -678,42 +671,49 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   const int v_op0 = lane_base(kV + SwizzledTile::operand_offset(lane, 0));
   const int v_op1 = lane_base(kV + SwizzledTile::operand_offset(lane, 1));
 
-  f32x16 sacc = f32x16{}, dpacc = f32x16{};  // S^T and dP^T of the tile between its phases
-  u32x4 pb[2];                               // dS^T of the previous tile, rounded (B operand)
-  pb[0] = pb[1] = u32x4{0, 0, 0, 0};
+  f32x16 sacc[2], dpacc[2];  // S^T and dP^T of each half of the tile between its phases
+  sacc[0] = sacc[1] = dpacc[0] = dpacc[1] = f32x16{};
+  u32x4 pb[4];               // dS^T of the previous tile, rounded (B operands)
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pb[u] = u32x4{0, 0, 0, 0};
 
-  // M phase on the tile in stage XS (S^T and dP^T chains) and the previous tile in stage YS
-  // (dQ^T chain), interleaved S, dP, dQ; each LDS operand read kAheadM MFMAs before its MFMA.
-  constexpr int kMfma = 3 * kSteps;
-  static_assert(2 * kOBlocks == kSteps, "one dQ MFMA per S MFMA");
+  // M phase on the tile in stage xs (S^T and dP^T chains of both halves) and the previous tile
+  // in stage ys (dQ^T chain): MFMA n is, by n % 3, S, dP (step s = n / 6 of half (n / 3) % 2)
+  // or dQ (MFMA n / 3: head-dim block % kOBlocks, 16-key step / kOBlocks); each LDS operand
+  // is read kAheadM MFMAs before its MFMA.
+  constexpr int kMfma = 6 * kSteps;
+  static_assert(4 * kOBlocks == 2 * kSteps, "one dQ MFMA per S MFMA");
   constexpr int kAheadM = 4;
   auto phase_m = [&](int xs, int ys) __attribute__((always_inline)) {
-    const int xo = xs * G::kTileBytes, yo = ys * G::kTileBytes;
+    const int xo = xs * kTBytes, yo = ys * kTBytes;
     const int ko0 = k_op0 + xo, ko1 = k_op1 + xo, vo0 = v_op0 + xo, vo1 = v_op1 + xo;
     const int kt0 = k_tr0 + yo, kt1 = k_tr1 + yo;
     u32x4 opnd[kMfma];
     auto fetch = [&](auto nn) __attribute__((always_inline)) {
-      constexpr int n = decltype(nn)::value, s = n / 3;
+      constexpr int n = decltype(nn)::value, g = n / 3, hf = g % 2, s = g / 2;
       if constexpr (n % 3 == 0) {
-        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? ko1 : ko0) + s * 1024);
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? ko1 : ko0) +
+                                                  hf * kHalfBytes + s * 1024);
       } else if constexpr (n % 3 == 1) {
-        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? vo1 : vo0) + s * 1024);
+        opnd[n] = *reinterpret_cast<const u32x4*>(smem + ((s & 1) ? vo1 : vo0) +
+                                                  hf * kHalfBytes + s * 1024);
       } else {
-        constexpr int j = s % kOBlocks, tt = s / kOBlocks;
-        const u32x2 lo = E::read_tr(smem + kt0 + 2048 * j + 256 * tt);
-        const u32x2 hi = E::read_tr(smem + kt1 + 2048 * j + 256 * tt);
+        constexpr int j = g % kOBlocks, u = g / kOBlocks;
+        constexpr int off = (u / 2) * kHalfBytes + 2048 * j + 256 * (u % 2);
+        const u32x2 lo = E::read_tr(smem + kt0 + off);
+        const u32x2 hi = E::read_tr(smem + kt1 + off);
         opnd[n] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     };
     auto mfma = [&](auto nn) __attribute__((always_inline)) {
-      constexpr int n = decltype(nn)::value, s = n / 3;
+      constexpr int n = decltype(nn)::value, g = n / 3, hf = g % 2, s = g / 2;
       if constexpr (n % 3 == 0) {
-        sacc = E::mfma(opnd[n], qf[s], s == 0 ? f32x16{} : sacc);
+        sacc[hf] = E::mfma(opnd[n], qf[s], s == 0 ? f32x16{} : sacc[hf]);
       } else if constexpr (n % 3 == 1) {
-        dpacc = E::mfma(opnd[n], dof[s], s == 0 ? f32x16{} : dpacc);
+        dpacc[hf] = E::mfma(opnd[n], dof[s], s == 0 ? f32x16{} : dpacc[hf]);
       } else {
-        constexpr int j = s % kOBlocks, tt = s / kOBlocks;
-        dqacc[j] = E::mfma(opnd[n], pb[tt], dqacc[j]);
+        constexpr int j = g % kOBlocks, u = g / kOBlocks;
+        dqacc[j] = E::mfma(opnd[n], pb[u], dqacc[j]);
       }
     };
     [&]<int... n>(std::integer_sequence<int, n...>) {
@@ -733,42 +733,44 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   // V phase of key tile `tile`: dS^T = P^T (dP^T - D), P^T = exp2(c S^T - log2(e) L), with
   // P = 0 where the key is past the end or above the diagonal; rounded into pb.
   auto phase_v = [&](int tile) __attribute__((always_inline)) {
-    const int r0 = tile * kTileRows;
-    // entry i is key r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
-    float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sacc[i], p.c, nlse);
-    if ((r0 + kTileRows > slen) || (CAUSAL && r0 + kTileRows - 1 > qw0)) {
-      // visible while off_i <= lim
-      const int lim = (CAUSAL ? min(slen - 1, qrow) : slen - 1) - r0 - 4 * half;
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r0 = tile * kKeysT + kTileRows * hf;
+      // entry i is key r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = 8 * (i >> 2) + (i & 3);
-        x[i] = off <= lim ? x[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) x[i] = fmaf(sacc[hf][i], p.c, nlse);
+      if ((r0 + kTileRows > slen) || (CAUSAL && r0 + kTileRows - 1 > qw0)) {
+        // visible while off_i <= lim
+        const int lim = (CAUSAL ? min(slen - 1, qrow) : slen - 1) - r0 - 4 * half;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 8 * (i >> 2) + (i & 3);
+          x[i] = off <= lim ? x[i] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = 8 * tt + 2 * w;
+          const float d0 = __builtin_amdgcn_exp2f(x[i]) * (dpacc[hf][i] - del);
+          const float d1 = __builtin_amdgcn_exp2f(x[i + 1]) * (dpacc[hf][i + 1] - del);
+          pb[2 * hf + tt][w] = E::pack(d0, d1);
+        }
     }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int i = 8 * tt + 2 * w;
-        const float d0 = __builtin_amdgcn_exp2f(x[i]) * (dpacc[i] - del);
-        const float d1 = __builtin_amdgcn_exp2f(x[i + 1]) * (dpacc[i + 1] - del);
-        pb[tt][w] = E::pack(d0, d1);
-      }
   };
 
-  // Slot 2t issues tile t + kAhead (into the stage of tile t - 2, last read by group 1's M(t-1)
-  // in slot 2t - 1); slot 2t + 1 ends by waiting for tile t + 1, which slot 2t + 2 reads. The
-  // loop runs t = 0 .. n_tiles: group 0's M(n_tiles) and group 1's M(n_tiles) only add
-  // dQ(n_tiles - 1) (their S and dP chains read a stale stage and are not used). The ring
-  // stage is a loop variable: unrolling the loop over the stages would keep more registers
-  // live than a wave has.
+  // Slot 2t issues tile t + 1 (into the stage of tile t - 2, last read by group 1's M(t-1) in
+  // slot 2t - 1); slot 2t + 1 ends by waiting for it (slot 2t + 2 reads it). The ring stage is
+  // a loop variable. The loop runs t = 0 .. n_tiles: M(0) of either group adds
+  // K(-1)^T dS^T(-1) = 0 (the stand-in stage is zero, pb starts at 0); M(n_tiles) of either
+  // group only adds dQ(n_tiles - 1) (its S and dP chains read a stale stage and are not used).
   auto run = [&](auto grp_c) __attribute__((always_inline)) {
     constexpr bool G1 = decltype(grp_c)::value;
-    int st = 0, st_prev = kRing - 1, st_issue = kAhead;  // stages of tiles t, t - 1, t + kAhead
+    int st = 0, st_prev = kRing - 1, st_next = 1;  // stages of tiles t, t - 1, t + 1
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t + kAhead < n_tiles) issue(st_issue);
+      if (t + 1 < n_tiles) issue(st_next);
       if constexpr (!G1) {
         phase_m(st, st_prev);
       } else {
@@ -780,11 +782,11 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
       } else {
         phase_m(st, st_prev);
       }
-      if (t + 1 < n_tiles) dma_wait(min(kAhead - 1, n_tiles - 2 - t));
+      if (t + 1 < n_tiles) wait_vmcnt<0>();  // tile t + 1
       phase_sync();
       st_prev = st;
-      st = st == kRing - 1 ? 0 : st + 1;
-      st_issue = st_issue == kRing - 1 ? 0 : st_issue + 1;
+      st = st_next;
+      st_next = st_next == kRing - 1 ? 0 : st_next + 1;
     }
   };
 
@@ -792,10 +794,10 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
     // The K stage kRing - 1 stands in for tile -1 until tile kRing - 1 lands there: zeros, so
     // that dQ^T += K(-1)^T dS^T(-1) with dS^T(-1) = 0 adds 0.
     const u32x4 zero = u32x4{0, 0, 0, 0};
-    for (int off = tid * 16; off < G::kTileBytes; off += kThreads8 * 16)
-      *reinterpret_cast<u32x4*>(smem + kK + (kRing - 1) * G::kTileBytes + off) = zero;
+    for (int off = tid * 16; off < kTBytes; off += kThreads8 * 16)
+      *reinterpret_cast<u32x4*>(smem + kK + (kRing - 1) * kTBytes + off) = zero;
   }
-  for (int x = 0; x < kAhead && x < n_tiles; ++x) issue(x);
+  if (n_tiles > 0) issue(0);
   // tile 0 and the resident operands complete; the empty asm makes the compiler's own load
   // tracking agree, so that it adds no memory waits inside the loop
   wait_vmcnt<0>();
