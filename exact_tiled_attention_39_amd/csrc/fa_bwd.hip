@@ -78,6 +78,42 @@ struct BwdArgs {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Single-copy layout of a 32-row tile (rows are queries or keys, head-dim contiguous in device
+// memory), for a tensor that is read both ways: as the operand of a contraction over head-dims
+// and, through ds_read_b64_tr_b16, as the A operand of a contraction over rows. Block s (1 KB)
+// holds head-dims 16 s .. 16 s + 15 of the 32 rows as 64 chunks of 16 bytes; chunk (r, c) is
+// row r, head-dims 16 s + 8 c .. + 7, and sits at chunk position
+//     16 (r / 16 + 2 c) + r % 4 + 4 ((r / 4 + c + 2 (s % 2)) % 4).
+// The rotation of the 4-row group index by c and by the block parity spreads both read
+// patterns over all LDS banks: 16 lanes of an operand read hit 16 distinct 16-byte slots of a
+// 256-byte bank row, and 32 lanes of a transposing read hit 32 distinct 8-byte slots.
+struct SwizzledTile {
+  // The chunk that lane L of a direct-to-LDS load into block s receives (its position is L).
+  static __device__ __forceinline__ void row_col(int s, int lane, int& row, int& col) {
+    const int hi = lane >> 4, lo = lane & 15;
+    const int c = hi >> 1;
+    row = 16 * (hi & 1) + 4 * (((lo >> 2) - c - 2 * (s & 1)) & 3) + (lo & 3);
+    col = 16 * s + 8 * c;
+  }
+  // Operand read: lane L takes chunk (L % 32, L / 32) of block s at byte s * 1024 + this
+  // offset (sp = s % 2).
+  static __device__ __forceinline__ int operand_offset(int lane, int sp) {
+    const int r = lane & 31, c = lane >> 5;
+    return 16 * (16 * ((r >> 4) + 2 * c) + (r & 3) + 4 * (((r >> 2) + c + 2 * sp) & 3));
+  }
+  // Transposing reads of the A operand for head-dims 32 j .. 32 j + 31 and rows 16 t .. 16 t +
+  // 15: the read for rows {4 g .. 4 g + 3} (part 0) or {8 + 4 g .. 8 + 4 g + 3} (part 1) of
+  // half-wave g sits at byte 2048 j + 256 t + this offset. Lane L supplies 4 head-dims of one
+  // row: row 8 part + 4 (L / 32) + (L % 16) / 4 of the step, head-dims 32 j + 16 ((L / 16) % 2)
+  // + 4 (L % 4) .. + 3.
+  static __device__ __forceinline__ int transpose_offset(int lane, int part) {
+    const int g16 = lane >> 4, i = lane & 15;
+    const int c = (i >> 1) & 1, sp = g16 & 1;
+    return 1024 * sp + 512 * c + 16 * (i >> 2) + 64 * ((2 * part + (g16 >> 1) + c + 2 * sp) & 3) +
+           8 * (i & 1);
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // D = rowsum(dO * O), fp32. 16 lanes per row, 8 (d = 128) or 4 (d = 64) elements per lane.
 template <int D, bool BF16>
