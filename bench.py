@@ -59,7 +59,7 @@ def measured_traffic(workload: str, kernel: str = "fa_fwd"):
     text = path.read_text()
     src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    sources = SPLITKV_SOURCES if kernel == "fa_splitkv" else KERNEL_SOURCES
+    sources = {"fa_splitkv": SPLITKV_SOURCES, "fa_fwd_fp8": FP8_SOURCES}.get(kernel, KERNEL_SOURCES)
     if not src or not val or src.group(1) != kernel_source_hash(sources):
         return None
     return float(val.group(1))
@@ -465,7 +465,8 @@ def bench_fp8(args, torch, fa, w: si.Workload) -> int:
     line["pct_of_peak"] = round(100.0 * value / peak, 2)
     line["roofline"] = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fa_fwd_fp8_kernel",
+        "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, "fa_fwd_fp8"),
+        "kernel": "fa_fwd_fp8_kernel",
         "avg_launch_ms": round(avg_ms, 4),
         "launch_ms_min_max": [round(min(launch_ms), 4), round(max(launch_ms), 4)],
         "launch_ms_p10_p50_p90": launch_percentiles(launch_ms),
