@@ -138,6 +138,11 @@ def cpu_baseline(w: si.Workload, inp, seconds: float, bytes_metric: bool = False
         "cores": len(os.sched_getaffinity(0)),
         "blas_threads": int(blas),
         "kind": "oracle",
+        "seconds": round(elapsed, 3),
+        "sample_fraction_of_flops": flops / w.flops(),
+        # the whole workload through the oracle at the sample's rate (FLOP-weighted rows)
+        "extrapolated_full_workload_s": round(elapsed * w.flops() / flops, 1) if flops else None,
+        "oracle_gflops_fp64": round(flops / elapsed / 1e9, 3) if elapsed else None,
         "sample": (f"{done} seeded query rows of {total_rows} ({done / total_rows:.2e} of the "
                    f"workload), 32 rows of one head per oracle call, {elapsed:.1f} s of oracle "
                    f"time (inputs decoded to fp64 beforehand, untimed), fp64, "

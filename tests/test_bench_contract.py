@@ -64,6 +64,11 @@ def test_headline_bench_line_carries_the_contract():
     assert cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
 
     assert cpu["blas_threads"] >= 1
+    # the extrapolation to the whole workload is the sample's time over its share of the FLOPs
+    assert 0.0 < cpu["sample_fraction_of_flops"] <= 1.0
+    assert cpu["extrapolated_full_workload_s"] == pytest.approx(
+        cpu["seconds"] / cpu["sample_fraction_of_flops"], rel=2e-2)
+    assert cpu["oracle_gflops_fp64"] == pytest.approx(cpu["value"] * 1e3, rel=2e-2)
 
     par = line["parity"]
     assert par["max_abs_dO"] <= 1.6e-2 and par["max_lse_err"] <= 1e-5
