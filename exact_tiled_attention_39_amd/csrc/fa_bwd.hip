@@ -13,14 +13,19 @@
 //  * fa_bwd_dkdv_kernel: one workgroup per 128 keys of a (batch entry or sequence, kv head).
 //    Each SIMD runs a dV wave and a dK wave for the same 32 keys, with K (dV wave) or V (dK
 //    wave) resident in registers as MFMA B operands and dV^T or dK^T accumulating in fp32.
-//    32-query tiles of Q and dO (of every query head that shares the kv head) stream through a
-//    three-stage LDS ring. The dV wave forms S = Q K^T and P of a tile, hands P to the dK wave
-//    through LDS and accumulates dV^T += dO^T P; the dK wave, one tile behind, forms
-//    dP = dO V^T, dS = P (dP - D) and accumulates dK^T += Q^T dS.
+//    64-query tiles of Q and dO (of every query head that shares the kv head) stream through a
+//    three-stage LDS ring. The two waves of a SIMD alternate between matrix and element-wise
+//    phases: the dV wave forms S = Q K^T and P of a tile, hands P to the dK wave through LDS
+//    and accumulates dV^T += dO^T P; the dK wave, one phase behind, forms dP = dO V^T,
+//    dS = P (dP - D) and accumulates dK^T += Q^T dS.
 //  * fa_bwd_dq_kernel: one workgroup per 256 queries of a (batch entry or sequence, query
 //    head). Its 8 waves own 32 queries each, with Q^T and dO^T resident, and dQ^T
-//    accumulating. 32-key tiles of K and V stream through double-buffered LDS. Per tile and
-//    wave: S^T = K Q^T and dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T.
+//    accumulating. 64-key tiles of K and V stream through a three-stage LDS ring. The two
+//    waves of a SIMD alternate between matrix phases (S^T = K Q^T and dP^T = V dO^T of a tile,
+//    lane = query, with dQ^T += K^T dS^T of the tile before) and element-wise phases (dS^T).
+//  * Q and dO (dK/dV) and K (dQ) are read both as operands of a contraction over head-dims and,
+//    transposed, of a contraction over the tile's rows; each tile is stored once in LDS, in a
+//    swizzled layout that serves both reads without bank conflicts.
 // Splitting dQ from dK/dV recomputes S and dP once more, but every gradient accumulates in
 // one workgroup's registers: no atomics, and the result is deterministic.
 // All MFMAs are v_mfma_f32_32x32x16_{bf16,f16}; P and dS are rounded to the input type (round
@@ -213,49 +218,11 @@ __device__ __forceinline__ void load_resident(const uint16_t* base, int64_t sn, 
 
 // ---------------------------------------------------------------------------------------
 // Both main kernels run 8 waves, two per SIMD, each wave within 256 registers, so that the
-// SIMD interleaves one wave's element-wise work with the other's matrix products. A tile of 32
-// rows of the streamed side moves through LDS per step (three stages for dK/dV, two for dQ).
+// SIMD overlaps one wave's element-wise phase with the other's matrix phase. A tile of 64 rows
+// of the streamed side moves through a three-stage LDS ring per step.
 
 constexpr int kWaves = 8;
 constexpr int kThreads8 = 64 * kWaves;
-
-// LDS operand reads of one tile for an MFMA chain over the head dimension: block s of a tile in
-// the operand layout (32 rows x 16 head-dims) at `base`.
-template <bool BF16, int kSteps>
-__device__ __forceinline__ f32x16 chain_over_d(const unsigned char* base, const u32x4* bop) {
-  using E = Elem<BF16>;
-  f32x16 acc = f32x16{};
-  u32x4 a[kSteps];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) a[s] = *reinterpret_cast<const u32x4*>(base + s * 1024);
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) acc = E::mfma(a[s], bop[s], acc);
-  return acc;
-}
-
-// acc[j] += (32 head-dims of block j) x (tile rows) . B, over the tile's two 16-row steps, with
-// the A operand from the transposing layout at `base` (block (t, j) at (t * kOBlocks + j) KB).
-template <bool BF16, int kOBlocks>
-__device__ __forceinline__ void chain_over_rows(const unsigned char* base, const u32x4 b[2],
-                                                f32x16* acc) {
-  using E = Elem<BF16>;
-  u32x4 a[2 * kOBlocks];
-#pragma unroll
-  for (int m = 0; m < 2 * kOBlocks; ++m) {
-    const u32x2 lo = E::read_tr(base + m * 1024);
-    const u32x2 hi = E::read_tr(base + m * 1024 + 512);
-    a[m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-  }
-#pragma unroll
-  for (int m = 0; m < 2 * kOBlocks; ++m) acc[m % kOBlocks] = E::mfma(a[m], b[m / kOBlocks],
-                                                                     acc[m % kOBlocks]);
-}
-
-__device__ __forceinline__ void tile_sync() {
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __syncthreads();
-}
 
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys. Waves 0-3 (one per SIMD) accumulate dV for 32 keys
