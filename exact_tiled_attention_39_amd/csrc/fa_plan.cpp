@@ -23,8 +23,9 @@ SplitPlan plan_splitkv(const fa_fwd_params& p, int32_t num_splits) {
     // workgroup pays a pipeline fill (its first tiles' full memory latency), so with equal
     // keys per sequence one round of equal workgroups is best (measured: 1 round 189 us, 2
     // rounds 201 us, 4 rounds 221 us for 16 sequences x 8 kv heads x 16K keys). Packed
-    // sequences of unequal lengths take two rounds, which lets the short splits fill in
-    // around the long ones. At least four tiles (128 keys) per split.
+    // sequences of unequal lengths take two rounds: the split kernel starts the longest
+    // sequences' splits first and the short splits fill in behind them. At least four tiles
+    // (128 keys) per split.
     constexpr int64_t kResident = 256 * 3;
     const int64_t rounds = varlen ? 2 : 1;
     const int64_t units = std::max<int64_t>(groups * p.heads_kv * plan.rowblocks, 1);

@@ -11,12 +11,13 @@
 //    read once for the whole head group (the GQA layout of the "Flash Attention" notes,
 //    section "Flash Attention 2 Improvements").
 //  * Split keys: the key tiles of each (sequence, kv head, row block) are divided into
-//    `splits` contiguous ranges, one workgroup each. A split runs the online softmax of the
-//    notes' Theorem 2 over its range and writes its normalised partial output O_z and its
-//    log-sum-exp L_z (log2 units) to the caller's workspace. The merge kernel then applies the
-//    same rescaling rule once more across splits: M = max_z L_z, w_z = 2^(L_z - M),
-//    O = sum_z w_z O_z / sum_z w_z, LSE = M + log2(sum_z w_z). With one split the first kernel
-//    writes O and LSE itself.
+//    `splits` contiguous ranges, one workgroup each; packed sequences (up to 64) are taken
+//    longest first, so that short ranges fill in behind the long ones. A split runs the
+//    online softmax of the notes' Theorem 2 over its range and writes its normalised partial
+//    output O_z and its log-sum-exp L_z (log2 units) to the caller's workspace. The merge
+//    kernel then applies the same rescaling rule once more across splits: M = max_z L_z,
+//    w_z = 2^(L_z - M), O = sum_z w_z O_z / sum_z w_z, LSE = M + log2(sum_z w_z). With one
+//    split the first kernel writes O and LSE itself.
 //  * One wave per workgroup with a private three-stage ring of 32-key K/V tiles in LDS, filled
 //    by direct-to-LDS loads two tiles ahead: no barriers, and the three workgroups an LDS of
 //    160 KB holds per CU keep about 100 KB of loads in flight per CU.
@@ -73,6 +74,7 @@ struct SplitArgs {
   int32_t n_rowblocks;  // 32-row blocks per (sequence, kv head)
   int32_t splits;
   int32_t items;        // splits * heads_kv * (batch or sequences)
+  int32_t num_seqs;     // packed sequences (with cu_seqlens)
   float c;              // |scale| * log2(e), or log2(e) when scale == 0
   uint32_t q_and;       // 0 when scale == 0, else all ones
   uint32_t q_xor;       // 0x80008000 when scale < 0 (Q negated exactly)
@@ -118,7 +120,20 @@ void fa_splitkv_kernel(const SplitArgs p) {
   const int z = item % p.splits;
   const int gb = item / p.splits;
   const int g = gb % p.heads_kv;
-  const int b = gb / p.heads_kv;
+  int b = gb / p.heads_kv;
+  if (VARLEN && p.num_seqs <= 64 && p.splits > 1) {
+    // Packed sequences of unequal lengths: item block b runs the sequence with the b-th most
+    // keys (ties by index), so the longest ranges start first and the short ones fill in
+    // behind them. Lane s holds sequence s's key count and counts the sequences ahead of it.
+    const int len = lane < p.num_seqs ? p.cu_seqlens_k[lane + 1] - p.cu_seqlens_k[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < p.num_seqs; ++j) {
+      const int lj = __shfl(len, j);
+      rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < p.num_seqs && rank == b);
+    b = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(hit)));
+  }
 
   int seq0 = 0, slen = p.seqlen, kseq0 = 0, klen = p.seqlen_k, bidx = b;
   if (VARLEN) {
@@ -478,6 +493,7 @@ fa_status launch_forward_splitkv(const fa_fwd_params& p, const SplitPlan& plan, 
   a.n_rowblocks = int32_t(plan.rowblocks);
   a.splits = plan.splits;
   a.items = int32_t(plan.items);
+  a.num_seqs = p.cu_seqlens != nullptr ? p.num_seqs : 0;
   const double c = (p.scale == 0.f ? 1.0 : std::fabs(double(p.scale))) * 1.4426950408889634;
   a.c = float(c);
   a.q_and = p.scale == 0.f ? 0u : 0xFFFFFFFFu;
