@@ -138,3 +138,19 @@ def test_split_count_changes_only_rounding():
     for splits in (1, 2, 13, 64, 157):
         o, lse = run(inp, splits=splits)
         assert_close(o, lse, o_ref, lse_ref, si.F16, f"splits={splits}")
+
+
+@pytest.mark.parametrize("n_seqs", [64, 65])
+@pytest.mark.parametrize("splits", [0, 5])
+def test_many_packed_sequences_with_tied_lengths(n_seqs, splits):
+    """Up to 64 packed sequences run longest first (ties by index); more run in launch order.
+    Both orders cover every (sequence, kv head, range) once: lengths with ties, zero-length
+    caches and sequences without queries, against the oracle."""
+    rng = np.random.default_rng(640 + n_seqs)
+    lens_k = [int(x) for x in rng.choice([0, 31, 32, 300, 300, 300, 777, 1500], size=n_seqs)]
+    lens_q = [int(x) for x in rng.choice([0, 1, 1, 2], size=n_seqs)]
+    inp = si.random_inputs(1, 4, 2, sum(lens_q), 64, si.F16, seed=641, causal=True,
+                           seq_lens=tuple(lens_q), seqlen_k=sum(lens_k), seq_lens_k=tuple(lens_k))
+    o, lse = run(inp, splits=splits)
+    o_ref, lse_ref = _oracle(inp)
+    assert_close(o, lse, o_ref, lse_ref, si.F16, f"{n_seqs} packed sequences, splits={splits}")
