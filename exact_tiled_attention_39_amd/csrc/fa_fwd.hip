@@ -422,6 +422,8 @@ void fa_fwd_kernel(const KernelArgs p) {
     __builtin_amdgcn_s_setprio(0);
   };
 
+  constexpr bool kMidBarrier = D == 64;  // see the schedule below
+
   // Phase boundary: this wave's LDS reads are complete, then a workgroup barrier that the
   // instruction scheduler may not move register-only work across.
   auto phase_sync = [&]() __attribute__((always_inline)) {
@@ -432,16 +434,21 @@ void fa_fwd_kernel(const KernelArgs p) {
   };
 
   // ---- ping-pong schedule over ring stages ---------------------------------------------
-  // Slot 2p:   group 0 runs M(p),   group 1 runs V(p - 1)
-  // Slot 2p+1: group 0 runs V(p),   group 1 runs M(p)
+  // Step p: group 0 runs M(p), then V(p); group 1 runs V(p - 1), then M(p). Each step ends
+  // with a barrier; at d = 64 a second barrier between the two halves keeps the groups in
+  // opposite phases (slot 2p: M(p) beside V(p - 1); slot 2p + 1: V(p) beside M(p)). At
+  // d = 128 the groups drift within a step, which measured slightly faster on causal shapes
+  // and 4 % slower at d = 64; the ring needs only the barrier that ends each step.
   // M(p) reads K_p (stage p % 4) and V_{p-1} (stage (p - 1) % 4).
-  // K_p is read in slots 2p, 2p + 1; group 0 issues K_{p+3} in slot 2p + 1 and has waited
-  // for K_{p+1} before that slot's closing barrier.
-  // V_p is read in slots 2p + 2, 2p + 3; group 1 issues V_{p+2} in slot 2p and has waited
-  // for V_p before the closing barrier of slot 2p + 1.
-  // Both groups execute 2 (n_tiles + 1) barriers after the prologue's one. A block whose
-  // rows see no key at all (n_tiles == 0, only possible when keys are fewer than queries)
-  // skips the loop as a whole workgroup.
+  // K_p is read in step p (the M(p) of both groups); group 0 issues K_{p+3} after its M(p),
+  // into the stage of K_{p-1}, whose readers (the M(p - 1) of both groups) ended before step
+  // p began, and has waited for K_{p+1} before step p's closing barrier.
+  // V_p is read in step p + 1; group 1 issues V_{p+2} at the start of step p, into the stage
+  // of V_{p-2}, whose readers (the M(p - 1) of both groups) ended before step p began, and
+  // has waited for V_p before step p's closing barrier.
+  // Both groups execute the same barriers: n_tiles + 1 steps after the prologue's one (two
+  // per step at d = 64). A block whose rows see no key at all (n_tiles == 0, only possible
+  // when keys are fewer than queries) skips the loop as a whole workgroup.
   if (n_tiles > 0) {
     {
       // V stage 3 is read (with P = 0) before any tile lands there: it must hold finite data.
@@ -464,7 +471,7 @@ void fa_fwd_kernel(const KernelArgs p) {
     auto step_g0 = [&](auto st, int tile) __attribute__((always_inline)) {
       constexpr int ST = decltype(st)::value;
       phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
-      phase_sync();
+      if constexpr (kMidBarrier) phase_sync();
       if (tile < n_tiles) softmax(tile);
       if (tile + 3 < n_tiles) dma(Int<(ST + 3) & 3>{}, tile + 3);
       if (tile + 1 < n_tiles) dma_wait(min(n_tiles - 2 - tile, 2));  // K_{tile+1} in LDS
@@ -474,7 +481,7 @@ void fa_fwd_kernel(const KernelArgs p) {
       constexpr int ST = decltype(st)::value;
       if (tile >= 1) softmax(tile - 1);
       if (tile + 2 < n_tiles) dma(Int<(ST + 2) & 3>{}, tile + 2);
-      phase_sync();
+      if constexpr (kMidBarrier) phase_sync();
       phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
       if (tile < n_tiles) dma_wait(min(n_tiles - 1 - tile, 2));  // V_tile in LDS
       phase_sync();
