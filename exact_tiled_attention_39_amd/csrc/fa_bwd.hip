@@ -567,7 +567,10 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 // an M phase, M(t): S^T(t) = K(t) Q^T and dP^T(t) = V(t) dO^T interleaved with
 // dQ^T += K(t-1)^T dS^T(t-1), and a V phase, V(t): dS^T(t) = P^T(t) (dP^T(t) - D) with
 // P^T(t) = exp2(c S^T(t) - log2(e) L) (masked), rounded as the next M phase's B operand.
-// Slot 2t: group 0 runs M(t), group 1 V(t-1); slot 2t+1: group 0 runs V(t), group 1 M(t).
+// Step t: group 0 runs M(t), then V(t); group 1 runs V(t-1), then M(t). A barrier ends each
+// step; at d = 64 a second one between the halves holds the groups in opposite phases (slot
+// 2t: M(t) beside V(t-1); slot 2t+1: V(t) beside M(t)), while at d = 128 the groups may drift
+// within a step (1-3 % faster there, slower at d = 64, the same bits).
 // K and V tiles stream through a three-stage LDS ring by direct-to-LDS loads issued one tile
 // ahead; each is stored once, in the swizzled layout (K serves both its operand and its
 // transposing reads).
@@ -764,9 +767,10 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
     }
   };
 
-  // Slot 2t issues tile t + 1 (into the stage of tile t - 2, last read by group 1's M(t-1) in
-  // slot 2t - 1); slot 2t + 1 ends by waiting for it (slot 2t + 2 reads it). The ring stage is
-  // a loop variable. The loop runs t = 0 .. n_tiles: M(0) of either group adds
+  // Step t starts by issuing tile t + 1 (into the stage of tile t - 2, last read by the M(t-1)
+  // of both groups in step t - 1) and ends by waiting for it (step t + 1 reads it); no wave
+  // reads another's data, so the ring needs only the barrier that ends each step. The ring
+  // stage is a loop variable. The loop runs t = 0 .. n_tiles: M(0) of either group adds
   // K(-1)^T dS^T(-1) = 0 (the stand-in stage is zero, pb starts at 0); M(n_tiles) of either
   // group only adds dQ(n_tiles - 1) (its S and dP chains read a stale stage and are not used).
   auto run = [&](auto grp_c) __attribute__((always_inline)) {
@@ -779,7 +783,7 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
       } else {
         if (t >= 1) phase_v(t - 1);
       }
-      phase_sync();
+      if constexpr (D == 64) phase_sync();  // the two halves of a step (see above)
       if constexpr (!G1) {
         if (t < n_tiles) phase_v(t);
       } else {
