@@ -285,6 +285,8 @@ void fa_fwd_kernel(const KernelArgs p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) pb[kb][tt] = u32x4{0, 0, 0, 0};
 
+  constexpr bool kMidBarrier = D == 64;  // see the schedule below
+
   // M phase (matrix cores), straight-line: S of tile p from K stage KS, and P V of tile p - 1
   // from V stage VS. Before the first tile P is zero and the V stage holds zeros; after the
   // last tile the S result is never used.
@@ -306,6 +308,7 @@ void fa_fwd_kernel(const KernelArgs p) {
   auto phase_m = [&](auto ks, auto vs) __attribute__((always_inline)) {
     constexpr int KS = decltype(ks)::value;
     constexpr int VS = decltype(vs)::value;
+    if constexpr (!kMidBarrier) __builtin_amdgcn_s_setprio(1);  // see the softmax's priority
     u32x4 opnd[kMfma];
     auto fetch = [&](auto nn) __attribute__((always_inline)) {
       constexpr int n = decltype(nn)::value;
@@ -343,14 +346,16 @@ void fa_fwd_kernel(const KernelArgs p) {
            }()),
        ...);
     }(std::make_integer_sequence<int, kMfma>{});
+    if constexpr (!kMidBarrier) __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of S_tile (Theorem 2) into P_tile. Keys this wave cannot see (past the
   // sequence end, above the diagonal) get P = 0.
-  // The softmax wave issues ahead of the matrix wave on its SIMD: the V phase, not the MFMA
-  // chain, is the longer of the two.
+  // Issue priority: with two barriers per step (d = 64) the softmax wave issues ahead of the
+  // matrix wave on its SIMD, as the V phase is the longer of the two; with one barrier per
+  // step (d = 128) the matrix wave does (measured 0.3-0.6 % faster than either of the others).
   auto softmax = [&](int tile) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (kMidBarrier) __builtin_amdgcn_s_setprio(1);
     const int key0 = tile * kBlockN;
     const bool edge = (key0 + kBlockN > klen) || (CAUSAL && key0 + kBlockN - 1 > wrow0 + shift);
     if (edge) {
@@ -419,10 +424,8 @@ void fa_fwd_kernel(const KernelArgs p) {
           pb[kb][tt][e] = E::pack(ex[kb][8 * tt + 2 * e], ex[kb][8 * tt + 2 * e + 1]);
           lr_run[e] = E::add_pair(pb[kb][tt][e], lr_run[e]);
         }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (kMidBarrier) __builtin_amdgcn_s_setprio(0);
   };
-
-  constexpr bool kMidBarrier = D == 64;  // see the schedule below
 
   // Phase boundary: this wave's LDS reads are complete, then a workgroup barrier that the
   // instruction scheduler may not move register-only work across.
