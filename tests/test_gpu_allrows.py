@@ -3,7 +3,7 @@
 The 16K causal headline (32 heads), the 32K grouped-query workload (32 query heads over 8
 key/value heads) and the packed variable-length workload (16 sequences, 16 heads) are run once
 through the C-ABI; then every query row of every head is recomputed by the oracle and compared
-element by element, with the benchmark spec's tolerances (bf16: max |dO| <= 1.6e-2 per element; LSE:
+element by element, with the forward's tolerances (bf16: max |dO| <= 1.6e-2 per element; LSE:
 |dLSE| / max(|LSE|, 1) <= 1e-5 per row).
 
 Row blocks [r0, r1) of a causal sequence are evaluated as the oracle's query chunk of r1 - r0
