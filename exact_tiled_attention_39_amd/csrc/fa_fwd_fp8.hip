@@ -294,14 +294,6 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
 #pragma unroll
     for (int i = 0; i < kDma; ++i) dma16(rsrc, dst + i * 1024, ld_voff[i]);
   };
-  auto dma_wait = [&](int after) __attribute__((always_inline)) {
-    if (after >= 2)
-      wait_vmcnt<2 * kDma>();
-    else if (after == 1)
-      wait_vmcnt<kDma>();
-    else
-      wait_vmcnt<0>();
-  };
 
   const unsigned char* rd_k = lds_k + lane * 16;
   const unsigned char* rd_v = lds_v + lane * 8;
@@ -459,57 +451,67 @@ void fa_fwd_fp8_kernel(const Fp8Args p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- ping-pong schedule (the forward kernel's at d = 128) -------------------------------
-  // Step p: group 0 runs M(p), then V(p); group 1 runs V(p - 1), then M(p); one barrier ends
-  // each step, which is all the ring needs. The matrix phase is much the shorter here, and
-  // without a barrier between the halves the two groups' softmax phases overlap: 5-7 %
-  // faster than two barriers per step, with the same results.
+  // ---- ping-pong schedule --------------------------------------------------------------
+  // Step p: group 0 runs M(p), then V(p); group 1 runs V(p - 1), then M(p). Two steps share
+  // one barrier (double step p, p even, runs tiles p and p + 1). The matrix phase is much the
+  // shorter here; with fewer barriers the two groups drift and their softmax phases overlap:
+  // one barrier per step measured 5-7 % faster than two, and one per two steps another 1 %
+  // at d = 128 and 12 % at d = 64, with the same results.
+  // Ring: double step p reads K_p, K_{p+1} and V_{p-1}, V_p (stages p % 4 and p % 4 + 1, and
+  // (p - 1) % 4 and p % 4), and loads the next double step's K_{p+2}, K_{p+3} (group 0) and
+  // V_{p+1}, V_{p+2} (group 1) into the stages the previous double step read; each group
+  // waits for its own loads before the closing barrier.
   if (n_tiles > 0) {
     {
       const u32x4 zero = u32x4{0, 0, 0, 0};
       for (int off = tid * 16; off < G::kVBytes; off += kThreads * 16)
         *reinterpret_cast<u32x4*>(lds_v + 3 * G::kVBytes + off) = zero;
     }
+    // K_0, K_1 and V_0 are ready at the start of double step 0 (V stage 3 stands in for V_{-1})
     if (grp == 0) {
       dma(Int<0>{}, 0);
       if (n_tiles > 1) dma(Int<1>{}, 1);
-      if (n_tiles > 2) dma(Int<2>{}, 2);
-      dma_wait(min(n_tiles - 1, 2));
     } else {
       dma(Int<0>{}, 0);
-      if (n_tiles > 1) dma(Int<1>{}, 1);
     }
+    wait_vmcnt<0>();
     __syncthreads();
 
-    auto step_g0 = [&](auto st, int tile) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st)::value;
-      phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
-      if (tile < n_tiles) softmax(tile);
-      if (tile + 3 < n_tiles) dma(Int<(ST + 3) & 3>{}, tile + 3);
-      if (tile + 1 < n_tiles) dma_wait(min(n_tiles - 2 - tile, 2));
+    auto dstep_g0 = [&](auto st0, int p) __attribute__((always_inline)) {
+      constexpr int S0 = decltype(st0)::value;
+      phase_m(Int<S0>{}, Int<(S0 + 3) & 3>{});
+      if (p < n_tiles) softmax(p);
+      if (p + 2 < n_tiles) dma(Int<(S0 + 2) & 3>{}, p + 2);
+      if (p + 1 <= n_tiles) {
+        phase_m(Int<S0 + 1>{}, Int<S0>{});
+        if (p + 1 < n_tiles) softmax(p + 1);
+        if (p + 3 < n_tiles) dma(Int<(S0 + 3) & 3>{}, p + 3);
+      }
+      wait_vmcnt<0>();
       phase_sync();
     };
-    auto step_g1 = [&](auto st, int tile) __attribute__((always_inline)) {
-      constexpr int ST = decltype(st)::value;
-      if (tile >= 1) softmax(tile - 1);
-      if (tile + 2 < n_tiles) dma(Int<(ST + 2) & 3>{}, tile + 2);
-      phase_m(Int<ST>{}, Int<(ST + 3) & 3>{});
-      if (tile < n_tiles) dma_wait(min(n_tiles - 1 - tile, 2));
+    auto dstep_g1 = [&](auto st0, int p) __attribute__((always_inline)) {
+      constexpr int S0 = decltype(st0)::value;
+      if (p >= 1) softmax(p - 1);
+      if (p + 1 < n_tiles) dma(Int<(S0 + 1) & 3>{}, p + 1);
+      phase_m(Int<S0>{}, Int<(S0 + 3) & 3>{});
+      if (p + 1 <= n_tiles) {
+        softmax(p);
+        if (p + 2 < n_tiles) dma(Int<(S0 + 2) & 3>{}, p + 2);
+        phase_m(Int<S0 + 1>{}, Int<S0>{});
+      }
+      wait_vmcnt<0>();
       phase_sync();
     };
     if (grp == 0) {
-      for (int tile = 0; tile <= n_tiles; tile += 4) {
-        step_g0(Int<0>{}, tile);
-        if (tile + 1 <= n_tiles) step_g0(Int<1>{}, tile + 1);
-        if (tile + 2 <= n_tiles) step_g0(Int<2>{}, tile + 2);
-        if (tile + 3 <= n_tiles) step_g0(Int<3>{}, tile + 3);
+      for (int p = 0; p <= n_tiles; p += 4) {
+        dstep_g0(Int<0>{}, p);
+        if (p + 2 <= n_tiles) dstep_g0(Int<2>{}, p + 2);
       }
     } else {
-      for (int tile = 0; tile <= n_tiles; tile += 4) {
-        step_g1(Int<0>{}, tile);
-        if (tile + 1 <= n_tiles) step_g1(Int<1>{}, tile + 1);
-        if (tile + 2 <= n_tiles) step_g1(Int<2>{}, tile + 2);
-        if (tile + 3 <= n_tiles) step_g1(Int<3>{}, tile + 3);
+      for (int p = 0; p <= n_tiles; p += 4) {
+        dstep_g1(Int<0>{}, p);
+        if (p + 2 <= n_tiles) dstep_g1(Int<2>{}, p + 2);
       }
     }
   }
