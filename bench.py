@@ -154,8 +154,10 @@ def cpu_baseline(w: si.Workload, inp, seconds: float, bytes_metric: bool = False
 
 class ClockSampler:
     """Samples the GPU's shader clock (the active level of pp_dpm_sclk) and board power
-    (hwmon power1_input) from sysfs every 20 ms while the timed launches run. Reports null
-    fields where the files are not readable or several cards are visible."""
+    (hwmon power1_input) from sysfs every 5 ms while the timed launches run (instantaneous
+    readings: a short timed region holds few samples, and its first ones may precede the
+    clock's settling under load). Reports null fields where the files are not readable or
+    several cards are visible."""
 
     def __init__(self):
         import glob
@@ -188,7 +190,7 @@ class ClockSampler:
                         self.watts.append(float(f.read().strip()) / 1e6)
             except OSError:
                 pass
-            self._stop.wait(0.02)
+            self._stop.wait(0.005)
 
     def __enter__(self):
         self._thread.start()
