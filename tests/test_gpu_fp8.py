@@ -110,7 +110,7 @@ def _check(inp: si.Inputs8, what, unit_descales=False):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 129, 257, 520])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 129, 200, 257, 384, 448, 520])
 def test_shapes(n, d, causal):
     inp = si.random_inputs_fp8(2, 4, 2, n, d, seed=800 + n + d, causal=causal)
     _check(inp, f"fp8 n={n} d={d} causal={causal}")
