@@ -108,3 +108,26 @@ def test_backward_gradient_sums():
     assert np.all(np.abs(dk.sum(axis=2)) <= 2e-2 * scale_k)
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=0,
                                atol=2e-2 * np.abs(dv).sum(axis=2).max())
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [(si.BF16, 128, 8, 2), (si.F16, 64, 4, 4)])
+def test_backward_is_deterministic(dtype, d, hq, hkv):
+    """Every gradient accumulates in one workgroup's registers, in a fixed order: repeated calls
+    give the same bits (the two wave groups of a step may run out of phase, never out of order
+    on shared data). 3K tokens, causal, so that many ring steps run."""
+    import exact_tiled_attention_39_amd as fa
+
+    inp = si.random_inputs(1, hq, hkv, 3072, d, dtype, seed=91, causal=True)
+    dout = upload(si.random_output_grad(inp, seed=92), dtype)
+    q, k, v = (upload(x, dtype) for x in (inp.q, inp.k, inp.v))
+    o, lse = fa.attention(q, k, v, scale=inp.scale, causal=True)
+    first = None
+    for _ in range(4):
+        grads = fa.attention_backward(q, k, v, o, lse, dout, scale=inp.scale, causal=True)
+        torch.cuda.synchronize()
+        bits = [download_bits(g) for g in grads]
+        if first is None:
+            first = bits
+        else:
+            for a, b in zip(first, bits):
+                np.testing.assert_array_equal(a, b)
