@@ -516,7 +516,7 @@ def bench_backward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, up)
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, cu_seqlens=cu,
                           max_seqlen=max_seqlen)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    delta = torch.empty((2, *q.shape[:3]), dtype=torch.float32, device=dev)
 
     def step():
         fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, scale=w.scale, causal=w.causal,

@@ -28,7 +28,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libfa.so")
 FA_F16, FA_BF16, FA_E4M3 = 0, 1, 2
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_GQA,
  FA_ERR_VARLEN, FA_ERR_ABI, FA_ERR_LAUNCH, FA_ERR_SCRATCH) = range(10)
-FA_ABI_VERSION = 7
+FA_ABI_VERSION = 8
 FA_MAX_SPLITS = 256
 FA_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
@@ -508,9 +508,11 @@ def make_bwd_params(q, k, v, o, dout, lse, dq, dk, dv, delta, scale: float, caus
     for name in ("o", "dout", "dq"):
         if tuple(ts[name].shape) != tuple(q.shape):
             raise ValueError(f"{name} must match q")
-    for name, t in (("lse", lse), ("delta", delta)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (b, hq, n):
-            raise ValueError(f"{name} must be a contiguous float32 tensor [batch, heads_q, tokens]")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, hq, n):
+        raise ValueError("lse must be a contiguous float32 tensor [batch, heads_q, tokens]")
+    if (delta.dtype != torch.float32 or not delta.is_contiguous()
+            or tuple(delta.shape) != (2, b, hq, n)):
+        raise ValueError("delta must be a contiguous float32 workspace [2, batch, heads_q, tokens]")
     p = FaBwdParams(
         dtype=_DTYPES[q.dtype], q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
         dout=dout.data_ptr(), lse=lse.data_ptr(), delta=delta.data_ptr(), dq=dq.data_ptr(),
@@ -562,7 +564,7 @@ def attention_backward(q, k, v, o, lse, dout, *, scale: Optional[float] = None,
     dq = torch.empty_like(q, memory_format=torch.contiguous_format)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    delta = torch.empty((2, *q.shape[:3]), dtype=torch.float32, device=q.device)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, scale=scale, causal=causal,
            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
     return dq, dk, dv

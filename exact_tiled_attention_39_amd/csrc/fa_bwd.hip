@@ -9,7 +9,8 @@
 //     dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Three launches on the caller's stream:
-//  * fa_bwd_delta_kernel: D = rowsum(dO * O) in fp32 (into the caller's delta buffer).
+//  * fa_bwd_delta_kernel: D = rowsum(dO * O) in fp32, and -log2(e) L, into the caller's delta
+//    workspace (two arrays of batch x heads_q x seqlen floats).
 //  * fa_bwd_dkdv_kernel: one workgroup per 128 keys of a (batch entry or sequence, kv head).
 //    Each SIMD runs a dV wave and a dK wave for the same 32 keys, with K (dV wave) or V (dK
 //    wave) resident in registers as MFMA B operands and dV^T or dK^T accumulating in fp32.
@@ -55,7 +56,8 @@ struct BwdArgs {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float* delta;
+  float* delta;       // D, the first array of the caller's workspace
+  float* nlse;        // -log2(e) L, the second array
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -121,6 +123,8 @@ struct SwizzledTile {
 
 // ---------------------------------------------------------------------------------------
 // D = rowsum(dO * O), fp32. 16 lanes per row, 8 (d = 128) or 4 (d = 64) elements per lane.
+// The same pass writes -log2(e) L of every row, the offset the dK/dV kernel adds to c S: one
+// multiply per row here instead of one per score there.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const BwdArgs p) {
   using E = Elem<BF16>;
@@ -140,6 +144,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const BwdArgs p) {
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (part == 0 && row < p.rows_delta) p.delta[row] = acc;
+  if (part == 1 && row < p.rows_delta) p.nlse[row] = p.lse[row] * -kLog2e;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -253,9 +258,10 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   constexpr int kTBytes = 2 * G::kTileBytes;   // a 64-row tile of one tensor
   constexpr int kPer = 2 * G::kBlocks / 4;     // 1 KB blocks of its tensor a wave loads per tile
   constexpr int kRing = 3;
-  // Ring stage x of each tensor: Q tile at kQ + x kTBytes, dO tile at kDo + x kTBytes, 64 LSE
-  // at kRows + 2048 x and 64 D 1 KB after them (each a 1 KB direct-to-LDS load); each region
-  // spans less than 64 KB, so a per-lane base plus an immediate reaches every stage.
+  // Ring stage x of each tensor: Q tile at kQ + x kTBytes, dO tile at kDo + x kTBytes, 64
+  // values -log2(e) L at kRows + 2048 x and 64 D 1 KB after them (each a 1 KB direct-to-LDS
+  // load); each region spans less than 64 KB, so a per-lane base plus an immediate reaches
+  // every stage.
   constexpr int kQ = 0, kDo = kRing * kTBytes, kRows = 2 * kRing * kTBytes;
   constexpr int kPbuf = kRows + kRing * 2048;  // P of each key group: 64 rows x 32 keys fp32
   constexpr int kPwave = 2 * 4096;
@@ -288,8 +294,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
   const int n_steps = per_head * p.group;
 
   // DMA: waves 0-3 load the Q blocks of a tile, waves 4-7 the dO blocks, kPer each (block b is
-  // block b % kSteps of half b / kSteps); waves 0 and 1 also load the tile's 64 LSE and 64 D
-  // values (lanes 0..15 carry them, the rest read 0).
+  // block b % kSteps of half b / kSteps); waves 0 and 1 also load the tile's 64 -log2(e) L and
+  // 64 D values (lanes 0..15 carry them, the rest read 0).
   const bool is_do = role;
   const int64_t lay_sn = is_do ? p.do_sn : p.q_sn;
   const int64_t lay_sh = is_do ? p.do_sh : p.q_sh;
@@ -319,7 +325,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, base + i * 1024, ld_off[i]);
     if (wave < 2) {
-      const float* lsrc = wave == 0 ? p.lse + iss_lrow : p.delta + iss_lrow;
+      const float* lsrc = wave == 0 ? p.nlse + iss_lrow : p.delta + iss_lrow;
       dma16(make_rsrc(lsrc, rows * 4), lds0 + kRows + stage * 2048 + wave * 1024, lane * 16);
     }
     iss_src += src_step;
@@ -442,11 +448,11 @@ void fa_bwd_dkdv_kernel(const BwdArgs p) {
     for (int hf = 0; hf < 2; ++hf) {
       const int r0 = r0t + kTileRows * hf;
       // entry i is query row r0 + 4 half + off_i, off_i = 8 (i / 4) + i % 4
-      float lse[16], pv[16];
+      float nl[16], pv[16];
       read_rows16(reinterpret_cast<const float*>(smem + rows_rd + stage * 2048 + 128 * hf), 0,
-                  lse);
+                  nl);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = fmaf(xacc[hf][i], p.c, lse[i] * -kLog2e);
+      for (int i = 0; i < 16; ++i) pv[i] = fmaf(xacc[hf][i], p.c, nl[i]);
       if ((r0 + kTileRows > slen) || (CAUSAL && r0 < kw0 + 31)) {
         // the entry is visible when lo <= off_i <= hi (no row of a key past the end is)
         const int rbase = r0 + 4 * half;
@@ -623,7 +629,7 @@ void fa_bwd_dq_kernel(const BwdArgs p) {
   float nlse = 0.f, del = 0.f;  // -log2e LSE and D of this lane's query
   if (qrow < slen) {
     const int64_t r = (int64_t(bidx) * p.heads_q + h) * p.seqlen + seq0 + qrow;
-    nlse = -p.lse[r] * kLog2e;
+    nlse = p.nlse[r];
     del = p.delta[r];
   }
   f32x16 dqacc[kOBlocks];
@@ -884,6 +890,7 @@ fa_status launch_backward(const fa_bwd_params& p, void* stream, const char** hip
   a.n_kblocks = (rows + 127) / 128;
   a.n_qblocks = (rows + 255) / 256;
   a.rows_delta = p.batch * p.heads_q * p.seqlen;
+  a.nlse = p.delta + int64_t(a.rows_delta);
   a.c = float((p.scale == 0.f ? 1.0 : std::fabs(double(p.scale))) * 1.4426950408889634);
   a.s_and = p.scale == 0.f ? 0u : 0xFFFFFFFFu;
   a.s_xor = p.scale < 0.f ? 0x80008000u : 0u;

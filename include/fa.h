@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 /* Element type of Q, K, V and O. */
 typedef enum fa_dtype {
@@ -189,8 +189,10 @@ typedef struct fa_fwd_params {
  * Layouts are those of fa_fwd_params: q, o, dout, dq are [batch, heads_q, seqlen, head_dim];
  * k, v, dk, dv are [batch, heads_kv, seqlen, head_dim]; head_dim contiguous, the other strides
  * in elements. lse is fa_fwd's output for the same q, k, v, scale and mask (contiguous fp32
- * [batch, heads_q, seqlen]). delta is a caller-owned contiguous fp32 workspace of the same
- * shape that fa_bwd overwrites with D (libfa allocates nothing). dq, dk, dv are written in full
+ * [batch, heads_q, seqlen]). delta is a caller-owned contiguous fp32 workspace of two arrays of
+ * that shape ([2, batch, heads_q, seqlen], 8 * batch * heads_q * seqlen bytes) that fa_bwd
+ * overwrites: D in the first, -log2(e) * LSE in the second (the offset the dK/dV pass adds to
+ * each scaled score); libfa allocates nothing. dq, dk, dv are written in full
  * for every valid token, rounded to the input type from fp32 accumulators. Calls that may run
  * at the same time need their own delta buffers.
  */
@@ -203,7 +205,7 @@ typedef struct fa_bwd_params {
   const void* o;          /* fa_fwd's output */
   const void* dout;       /* dL/dO */
   const float* lse;       /* fa_fwd's log-sum-exp */
-  float* delta;           /* workspace, written */
+  float* delta;           /* workspace of 2 * batch * heads_q * seqlen floats, written */
   void* dq;
   void* dk;
   void* dv;

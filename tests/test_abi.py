@@ -296,6 +296,20 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     assert fa.fa_check_args(p) == fa.FA_OK
 
 
+def test_binding_backward_workspace_holds_two_arrays():
+    """The delta workspace holds D and the scaled LSE: [2, batch, heads_q, tokens] fp32."""
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    args = (q, q, q, q, q, lse, q, q, q)
+    with pytest.raises(ValueError, match="delta"):
+        fa.make_bwd_params(*args, torch.zeros(1, 2, 8), 0.1, False, None, None)
+    with pytest.raises(ValueError, match="delta"):
+        fa.make_bwd_params(*args, torch.zeros(2, 1, 2, 8, dtype=torch.float64), 0.1, False, None,
+                           None)
+    p = fa.make_bwd_params(*args, torch.zeros(2, 1, 2, 8), 0.1, False, None, None)
+    assert fa.fa_bwd_check_args(p) == fa.FA_OK
+
+
 def good_bwd(**kw):
     ptrs = dict(q=1, k=2, v=3, o=4, dout=5, lse=6, delta=7, dq=8, dk=9, dv=10)
     base = {name: ALIGNED * i for name, i in ptrs.items()}
