@@ -8,6 +8,10 @@ MI355X dense MFMA peak of the input type; and the fp64 CPU oracle timed on a bou
 sample of query rows of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+
+The default run (the headline workload) also times, after the headline and outside its timed
+region, the forward kernel on the other multi-tile workloads and the headline's backward pass,
+reported under "other_configs" (--no-other-configs skips them, as the profiler runs do).
 """
 from __future__ import annotations
 
@@ -352,6 +356,53 @@ def workload_config(w: si.Workload) -> dict:
             "num_seqs": len(w.seq_lens) if w.varlen else None}
 
 
+OTHER_FORWARD = ("b2_h8_n4096_d64_fp16", "gqa_b1_hq32_hkv8_n32768_d128_causal_bf16",
+                 "varlen16_h16_d128_causal_bf16")
+
+
+def other_configs(torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, o, lse) -> dict:
+    """Kernel time (HIP events, 5 warm-up and 20 timed calls) of fa_fwd on the other multi-tile
+    workloads and of fa_bwd on the headline workload, each on its own seeded inputs. Informative
+    only: none of it enters `value`."""
+    dev = q.device
+    out = {}
+    for name in OTHER_FORWARD:
+        ow = si.WORKLOADS[name]
+        oi = si.workload_inputs(ow)
+        tdt = torch.bfloat16 if ow.dtype == si.BF16 else torch.float16
+        oq, ok, ov = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev)
+                      for x in (oi.q, oi.k, oi.v))
+        oo = torch.empty_like(oq)
+        ol = torch.empty(oq.shape[:3], dtype=torch.float32, device=dev)
+        cu = torch.from_numpy(oi.cu_seqlens).to(dev) if ow.varlen else None
+        kw = dict(scale=ow.scale, causal=ow.causal, cu_seqlens=cu,
+                  max_seqlen=ow.max_seqlen() if ow.varlen else None)
+        _, ms = time_calls(torch, lambda: fa.fa_fwd(oq, ok, ov, oo, ol, **kw), 5, 20)
+        avg = float(np.mean(ms))
+        tf = ow.flops() / (avg * 1e-3) / 1e12
+        out[name] = {"pass": "forward", "avg_launch_ms": round(avg, 4), "tflops": round(tf, 2),
+                     "pct_of_peak": round(100.0 * tf / MFMA_PEAK_TFLOPS[ow.dtype], 2),
+                     "launch_ms_p10_p50_p90": launch_percentiles(ms)}
+        del oq, ok, ov, oo, ol, oi
+        torch.cuda.empty_cache()
+    tdt = q.dtype
+    do = torch.from_numpy(si.random_output_grad(inp, seed=w.seed + 100).view(np.int16)).view(
+        tdt).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((2, *q.shape[:3]), dtype=torch.float32, device=dev)
+    _, ms = time_calls(torch, lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta,
+                                                scale=w.scale, causal=w.causal), 5, 20)
+    avg = float(np.mean(ms))
+    tf = 2.5 * w.flops() / (avg * 1e-3) / 1e12
+    out[w.name] = {"pass": "backward (delta, dK/dV and dQ kernels; 2.5x the forward's FLOPs)",
+                   "avg_launch_ms": round(avg, 4), "tflops": round(tf, 2),
+                   "pct_of_peak": round(100.0 * tf / MFMA_PEAK_TFLOPS[w.dtype], 2),
+                   "launch_ms_p10_p50_p90": launch_percentiles(ms)}
+    del do, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> int:
     """fa_fwd over the workload; with --rope, RoPE on Q (as it is loaded) and K (the key pass)."""
     dev = q.device
@@ -430,6 +481,9 @@ def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
     line["kernel_source_sha256"] = kernel_source_hash()
     if not args.no_cpu_baseline:
         gpu.update(o_bits=bits(o, torch), lse=lse.cpu().numpy().astype(np.float64))
+    if w.name == si.HEADLINE and not args.rope and not args.no_other_configs:
+        line["other_configs"] = other_configs(torch, fa, w, inp, q, k, v, o, lse)
+    if not args.no_cpu_baseline:
         line.update(oracle_leg("forward", w, inp, gpu, args))
     print(json.dumps(line), flush=True)
     return 0
@@ -617,6 +671,9 @@ def main() -> int:
                     help="forward on E4M3 (FP8) inputs of the workload's shape")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of the workload instead of the forward")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the informative timings of the other workloads and of the "
+                         "backward pass that follow the headline forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 launches), the "
                          "known-size reference that scales the HBM byte counters")

@@ -83,3 +83,17 @@ def test_headline_bench_line_carries_the_contract():
     assert ex["achieved_per_s"] == pytest.approx(ex["exps_per_launch"] / (roof["avg_launch_ms"] * 1e-3),
                                                  rel=1e-3)
     assert "gpu_clocks" in line and "samples" in line["gpu_clocks"]
+
+    # the informative timings that follow the headline: the other multi-tile forward workloads
+    # and the headline's backward, none of them part of `value`
+    other = line["other_configs"]
+    assert set(other) == {"b2_h8_n4096_d64_fp16", "gqa_b1_hq32_hkv8_n32768_d128_causal_bf16",
+                          "varlen16_h16_d128_causal_bf16", si.HEADLINE}
+    assert other[si.HEADLINE]["pass"].startswith("backward")
+    for name, o in other.items():
+        assert 0.0 < o["tflops"] < 2500.0, name
+        assert o["pct_of_peak"] == pytest.approx(100.0 * o["tflops"] / 2500.0, abs=0.02), name
+        w = si.WORKLOADS[name]
+        mult = 2.5 if name == si.HEADLINE else 1.0
+        assert o["tflops"] == pytest.approx(mult * w.flops() / (o["avg_launch_ms"] * 1e-3) / 1e12,
+                                            rel=2e-3), name
