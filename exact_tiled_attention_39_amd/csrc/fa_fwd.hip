@@ -22,7 +22,8 @@
 //  * Ping-pong: the two wave groups alternate, one barrier-delimited phase apart, between an
 //    M phase (the S MFMAs of tile p and the P V MFMAs of tile p - 1) and a V phase (the online
 //    softmax of tile p), so each SIMD overlaps one wave's softmax with the other's matrix work.
-//    The softmax wave runs at the higher issue priority: its exp2 chain is the longer phase.
+//    At d = 64, where the softmax is the longer phase, the softmax wave runs at the higher
+//    issue priority; at d = 128 the matrix wave does (measured the faster choice for each).
 //  * K and V tiles of 64 keys stream into four-stage LDS rings by direct-to-LDS buffer loads
 //    (no staging registers, no LDS store instructions), issued two to three tiles ahead.
 //    Each tile is stored fragment-major: every 1 KB block holds exactly one MFMA operand in
