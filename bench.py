@@ -356,6 +356,28 @@ def workload_config(w: si.Workload) -> dict:
             "num_seqs": len(w.seq_lens) if w.varlen else None}
 
 
+def kv_stream_bytes(w: si.Workload, block_m: int = 256, block_n: int = 64) -> int:
+    """K and V bytes the forward kernel streams from L2/HBM into LDS per launch: every query
+    block of every (batch entry or sequence, query head) reads the K and V rows of the key
+    tiles it visits (64-key tiles, whole up to the last key; a causal block visits the tiles up
+    to its last row, with blocks aligned to the sequence end), each key row d elements of 2
+    bytes per tensor."""
+    if w.seq_lens is not None:
+        pairs = list(zip(w.seq_lens, w.seq_lens_k if w.seq_lens_k is not None else w.seq_lens))
+    else:
+        pairs = [(w.seqlen, w.keys)] * w.batch
+    rows = 0
+    for nq, nk in pairs:
+        shift = nk - nq
+        pad = (-nq) % block_m if w.causal else 0
+        for qb in range((nq + block_m - 1) // block_m):
+            q0 = block_m * qb - pad
+            kv_end = min(nk, q0 + block_m + shift) if w.causal else nk
+            if kv_end > 0:  # whole tiles up to kv_end; rows past the last key read nothing
+                rows += min((kv_end + block_n - 1) // block_n * block_n, nk)
+    return rows * w.heads_q * 2 * w.head_dim * 2
+
+
 OTHER_FORWARD = ("b2_h8_n4096_d64_fp16", "gqa_b1_hq32_hkv8_n32768_d128_causal_bf16",
                  "varlen16_h16_d128_causal_bf16")
 
@@ -476,6 +498,17 @@ def bench_forward(args, torch, fa, w: si.Workload, inp: si.Inputs, q, k, v) -> i
         "frac": round(exps / (avg_kernel_ms * 1e-3) / EXP2_PEAK_PER_S, 4),
         "note": "v_exp_f32 issue ceiling; the kernel also issues about 3 full-rate VALU "
                 "instructions per score (scale-and-shift FMA, row sums, conversion to the input type)",
+    }
+    # secondary volume: K/V rows streamed into LDS (re-read per query block and query head),
+    # served by L2 and the last-level cache; roofline.traffic is what reached HBM
+    kv = kv_stream_bytes(w)
+    traffic = line["roofline"]["traffic"]
+    line["kv_stream"] = {
+        "bytes_per_launch": kv,
+        "achieved_GBps": round(kv / (avg_kernel_ms * 1e-3) / 1e9, 1),
+        "hbm_bytes_over_stream_bytes": round(traffic / kv, 4) if traffic else None,
+        "note": "K and V tiles read into LDS by every 256-query block of every query head; "
+                "they come from L2 or the last-level cache, and the HBM traffic is a fraction of them",
     }
     line["gpu_clocks"] = time_calls.clocks
     line["kernel_source_sha256"] = kernel_source_hash()

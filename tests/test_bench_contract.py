@@ -23,6 +23,29 @@ def test_more_than_one_gpu_is_refused():
     assert not r.stdout.strip()
 
 
+def test_kv_stream_bytes_closed_forms():
+    """The K/V volume streamed into LDS, against closed forms of the 256 x 64 tiling."""
+    import bench
+    tile = 64 * 2 * 2  # one key row of K and V per head-dim element: 64 rows x 2 tensors x 2 B
+    # causal 16K, 32 heads: block b (256 queries) visits 4 (b + 1) tiles of 64 keys
+    w = si.WORKLOADS[si.HEADLINE]
+    assert bench.kv_stream_bytes(w) == 32 * sum(4 * (b + 1) for b in range(64)) * tile * 128
+    # non-causal: every block of every head reads all keys
+    w = si.WORKLOADS["b2_h8_n4096_d64_fp16"]
+    assert bench.kv_stream_bytes(w) == 2 * 8 * 16 * 4096 * 64 * 2 * 2
+    # GQA: the K/V of a kv head are read once per query head that shares it
+    w = si.WORKLOADS["gqa_b1_hq32_hkv8_n32768_d128_causal_bf16"]
+    assert bench.kv_stream_bytes(w) == 32 * sum(4 * (b + 1) for b in range(128)) * tile * 128
+    # a 2K query chunk at the end of 16K keys: block b visits the 14336 earlier keys plus its own
+    w = si.WORKLOADS["chunk_b1_hq32_hkv8_q2048_k16384_d128_causal_bf16"]
+    assert bench.kv_stream_bytes(w) == 32 * sum(14336 + 256 * (b + 1) for b in range(8)) * 128 * 4
+    # a causal sequence of 300 tokens: blocks aligned to its end (pad 212), so block 0 covers
+    # rows -212..43 (one tile) and block 1 rows 44..299 (all 300 keys, five tiles clamped at 300)
+    w = si.Workload(name="t", batch=1, heads_q=1, heads_kv=1, seqlen=300, head_dim=64,
+                    causal=True, dtype=si.F16, seed=0)
+    assert bench.kv_stream_bytes(w) == (64 + 300) * 64 * 2 * 2
+
+
 @pytest.mark.gpu
 def test_headline_bench_line_carries_the_contract():
     print("bench.py --steps 3 --warmup 1 --cpu-seconds 1 (headline workload)", flush=True)
@@ -83,6 +106,10 @@ def test_headline_bench_line_carries_the_contract():
     assert ex["achieved_per_s"] == pytest.approx(ex["exps_per_launch"] / (roof["avg_launch_ms"] * 1e-3),
                                                  rel=1e-3)
     assert "gpu_clocks" in line and "samples" in line["gpu_clocks"]
+    kv = line["kv_stream"]
+    assert kv["bytes_per_launch"] == 32 * sum(4 * (b + 1) for b in range(64)) * 64 * 4 * 128
+    assert kv["achieved_GBps"] == pytest.approx(
+        kv["bytes_per_launch"] / (roof["avg_launch_ms"] * 1e-3) / 1e9, rel=1e-3)
 
     # the informative timings that follow the headline: the other multi-tile forward workloads
     # and the headline's backward, none of them part of `value`
