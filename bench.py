@@ -383,9 +383,9 @@ OTHER_FORWARD = ("b2_h8_n4096_d64_fp16", "gqa_b1_hq32_hkv8_n32768_d128_causal_bf
 
 
 def other_configs(torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, o, lse) -> dict:
-    """Kernel time (HIP events, 5 warm-up and 20 timed calls) of fa_fwd on the other multi-tile
-    workloads and of fa_bwd on the headline workload, each on its own seeded inputs. Informative
-    only: none of it enters `value`."""
+    """Kernel time (HIP events, 5 warm-up and 20 timed calls, 100 for a workload of 0.1 ms calls)
+    of fa_fwd on the other multi-tile workloads and of fa_bwd on the headline workload, each on
+    its own seeded inputs. Informative only: none of it enters `value`."""
     dev = q.device
     out = {}
     for name in OTHER_FORWARD:
@@ -399,10 +399,12 @@ def other_configs(torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, o, lse) ->
         cu = torch.from_numpy(oi.cu_seqlens).to(dev) if ow.varlen else None
         kw = dict(scale=ow.scale, causal=ow.causal, cu_seqlens=cu,
                   max_seqlen=ow.max_seqlen() if ow.varlen else None)
-        _, ms = time_calls(torch, lambda: fa.fa_fwd(oq, ok, ov, oo, ol, **kw), 5, 20)
+        timed = 100 if ow.flops() < 1e11 else 20
+        _, ms = time_calls(torch, lambda: fa.fa_fwd(oq, ok, ov, oo, ol, **kw), 5, timed)
         avg = float(np.mean(ms))
         tf = ow.flops() / (avg * 1e-3) / 1e12
-        out[name] = {"pass": "forward", "avg_launch_ms": round(avg, 4), "tflops": round(tf, 2),
+        out[name] = {"pass": "forward", "timed_calls": timed, "avg_launch_ms": round(avg, 4),
+                     "tflops": round(tf, 2),
                      "pct_of_peak": round(100.0 * tf / MFMA_PEAK_TFLOPS[ow.dtype], 2),
                      "launch_ms_p10_p50_p90": launch_percentiles(ms)}
         del oq, ok, ov, oo, ol, oi
@@ -417,7 +419,7 @@ def other_configs(torch, fa, w: si.Workload, inp: si.Inputs, q, k, v, o, lse) ->
     avg = float(np.mean(ms))
     tf = 2.5 * w.flops() / (avg * 1e-3) / 1e12
     out[w.name] = {"pass": "backward (delta, dK/dV and dQ kernels; 2.5x the forward's FLOPs)",
-                   "avg_launch_ms": round(avg, 4), "tflops": round(tf, 2),
+                   "timed_calls": 20, "avg_launch_ms": round(avg, 4), "tflops": round(tf, 2),
                    "pct_of_peak": round(100.0 * tf / MFMA_PEAK_TFLOPS[w.dtype], 2),
                    "launch_ms_p10_p50_p90": launch_percentiles(ms)}
     del do, dq, dk, dv, delta
