@@ -131,3 +131,37 @@ def test_backward_is_deterministic(dtype, d, hq, hkv):
         else:
             for a, b in zip(first, bits):
                 np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_backward_workspace_contents(packed):
+    """fa_bwd's workspace after a call: D = rowsum(dO * O) per query row (against the fp64 sum
+    of the same dO and O values) in the first array, and -log2(e) * LSE in the second, the fp32
+    product of the forward's LSE, bit for bit."""
+    import exact_tiled_attention_39_amd as fa
+
+    if packed:
+        inp = si.random_inputs(1, 4, 2, 837, 128, si.BF16, seed=71, causal=True,
+                               seq_lens=(300, 17, 520))
+    else:
+        inp = si.random_inputs(2, 4, 2, 333, 64, si.F16, seed=72, causal=False)
+    dtype = inp.dtype
+    q, k, v = (upload(x, dtype) for x in (inp.q, inp.k, inp.v))
+    dout = upload(si.random_output_grad(inp, seed=73), dtype)
+    cu = torch.from_numpy(inp.cu_seqlens).cuda() if packed else None
+    max_seqlen = int(np.diff(inp.cu_seqlens).max()) if packed else None
+    o, lse = fa.attention(q, k, v, scale=inp.scale, causal=inp.causal, cu_seqlens=cu,
+                          max_seqlen=max_seqlen)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.full((2, *q.shape[:3]), float("nan"), dtype=torch.float32, device=q.device)
+    fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, scale=inp.scale, causal=inp.causal,
+              cu_seqlens=cu, max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    got = delta.cpu().numpy()
+    o64 = si.bits_to_f64(download_bits(o), dtype)
+    do64 = si.bits_to_f64(download_bits(dout), dtype)
+    d_ref = (o64 * do64).sum(axis=-1)
+    # fp32 sums of d products: within 1e-5 of the sum of their magnitudes
+    assert np.all(np.abs(got[0] - d_ref) <= 1e-5 * np.abs(o64 * do64).sum(axis=-1))
+    nlse = (lse.cpu() * torch.tensor(-1.4426950408889634, dtype=torch.float32)).numpy()
+    np.testing.assert_array_equal(got[1].view(np.uint32), nlse.view(np.uint32))
