@@ -397,7 +397,20 @@ void fa_fwd_kernel(const KernelArgs p) {
     // First tile: its own maximum is the reference (O and the sums are still zero). Every row
     // that sees any key sees one in the first tile of its sequence, so a row whose reference
     // stays -inf sees no key at all; its NaN sums take the rare path and are never stored.
-    if (tile == 0) m_run = tile_max();
+    if (tile == 0) {
+      if constexpr (D == 64) {
+        // the same maximum, formed in the opposite order: the compiler then keeps the rare
+        // path's first steps inside it instead of hoisting them into every tile
+        float mx = sacc[1][15];
+#pragma unroll
+        for (int kb = 1; kb >= 0; --kb)
+#pragma unroll
+          for (int i = 15; i >= 0; --i) mx = fmaxf(mx, sacc[kb][i]);
+        m_run = fmaxf(mx, __shfl_xor(mx, 32)) * p.c;
+      } else {
+        m_run = tile_max();
+      }
+    }
     expo(m_run);
     float rsum = (part[0] + part[1]) + (part[2] + part[3]);
     // Rare path: a score far above the reference. NaN sums also land here; they propagate to
