@@ -165,3 +165,16 @@ def test_backward_workspace_contents(packed):
     assert np.all(np.abs(got[0] - d_ref) <= 1e-5 * np.abs(o64 * do64).sum(axis=-1))
     nlse = (lse.cpu() * torch.tensor(-1.4426950408889634, dtype=torch.float32)).numpy()
     np.testing.assert_array_equal(got[1].view(np.uint32), nlse.view(np.uint32))
+
+
+def test_backward_packed_with_larger_max_seqlen_bound():
+    """max_seqlen only sizes the backward's grids: a loose upper bound (the packed total) gives
+    the same gradients, bit for bit, as the longest sequence."""
+    lens = (300, 17, 520, 64)
+    inp = si.random_inputs(1, 4, 2, sum(lens), 128, si.BF16, seed=81, causal=True, seq_lens=lens)
+    dout = si.random_output_grad(inp, seed=82)
+    tight = run_backward(inp, dout)
+    loose = run_backward(inp, dout, max_seqlen=sum(lens))
+    for a, b in zip(tight, loose):
+        np.testing.assert_array_equal(a, b)
+    assert_grads_close(tight, oracle_backward(inp, dout), si.BF16, "packed, loose max_seqlen")
